@@ -1,0 +1,185 @@
+/*
+ * w4a4.h -- C ABI of libw4a4: the SVDQuant W4A4 + 16-bit low-rank linear layer on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (SVDQuant summary page, arXiv 2411.05007v4, §4.2 and Fig. 4):
+ *
+ *     Y = Q(X̂) · Q(R)ᵀ + bf16(bf16(X̂) · L1) · L2 (+ bias),   X̂ = X · diag(λ)^-1
+ *     Ŵ = W · diag(λ),  Ŵᵀ ≈ L1 · L2 (rank r),  R = Ŵ − (L1 · L2)ᵀ
+ *
+ * λ are per-input-channel smoothing factors (App. D, after SmoothQuant), L1·L2 the rank-r SVD
+ * of the smoothed weight kept in 16 bits, Q a 4-bit quantizer: per-group (64 along K) symmetric
+ * INT4 with bf16 scales (App. D), or FP4 E2M1 with one power-of-two (E8M0) scale per block of 32.
+ * Following §4.3 / Fig. 6 the down projection X̂·L1 is computed by the activation quantizer and
+ * the up projection is added inside the 4-bit GEMM.
+ *
+ * Conventions
+ *  - Ownership: the caller allocates and frees every buffer; host buffers are ordinary arrays,
+ *    device buffers are device memory (e.g. from torch). The library never allocates device
+ *    memory, never synchronizes a stream and keeps no mutable global state.
+ *  - bf16 tensors are passed as uint16_t bit patterns. Row-major everywhere.
+ *  - Library layouts: codes and scales of activations and weights, and the low-rank factors, use
+ *    the private layouts described at w4a4_buffer_sizes(). Rows (M of X, N of W) are padded to a
+ *    multiple of W4A4_ROW_ALIGN; padding rows are written as zero codes with zero scales.
+ *    w4a4_codes_to_canonical() / w4a4_scales_to_canonical() convert to plain layouts.
+ *  - Errors: every argument is validated on the host before anything is launched or written;
+ *    a failed check returns a status and leaves outputs untouched. Device calls return
+ *    W4A4_ERR_HIP if a launch fails; faults inside kernels surface at the caller's stream
+ *    synchronization. No C++ exception crosses the ABI.
+ *  - Inputs are assumed finite. Device pointers must be 16-byte aligned.
+ */
+#ifndef W4A4_H
+#define W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A4_ABI_VERSION 1
+#define W4A4_GROUP 64        /* INT4 group size along K (App. D) */
+#define W4A4_MX_BLOCK 32     /* FP4 block size along K */
+#define W4A4_ROW_ALIGN 256   /* M and N are padded to a multiple of this in library layouts */
+#define W4A4_RANK_ALIGN 16   /* rank is zero-padded to a multiple of this (r_pad) */
+#define W4A4_MAX_RANK 128    /* largest supported rank (after any LoRA merge) */
+
+typedef enum {
+  W4A4_OK = 0,
+  W4A4_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment, rank out of range ... */
+  W4A4_ERR_UNSUPPORTED = 2,  /* unknown format */
+  W4A4_ERR_NUMERIC = 3,      /* non-finite / non-normal smoothing factor, SVD failure */
+  W4A4_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} w4a4_status_t;
+
+typedef enum {
+  W4A4_FMT_INT4_G64 = 0,     /* per-group-64 symmetric INT4, bf16 scales */
+  W4A4_FMT_MXFP4_B32 = 1     /* E2M1 codes, E8M0 scale per block of 32 */
+} w4a4_fmt_t;
+
+/* Same object as hipStream_t; NULL is the default stream. */
+typedef struct ihipStream_t* w4a4_stream_t;
+
+/* Byte sizes of every library buffer for one layer (see w4a4_buffer_sizes). */
+typedef struct {
+  size_t wq, wscale, l1t, l2t;   /* weights side (prepare_weights outputs) */
+  size_t xq, xscale, xl1;        /* activation side (quantize_act outputs) */
+  int m_pad, n_pad, rank_pad;
+} w4a4_sizes_t;
+
+int w4a4_abi_version(void);
+const char* w4a4_status_str(w4a4_status_t status);
+
+/*
+ * Buffer sizes and layouts. K must be a positive multiple of 64 for both formats (the MXFP4
+ * kernels step K by two 32-blocks). m_pad = roundup(M, 256), n_pad = roundup(N, 256),
+ * rank_pad = roundup(rank, 16) (0 for rank 0). Layouts (G64 = K/64, B32 = K/32):
+ *   wq     [G64][n_pad][32] bytes : the 64 codes of (row, group); code k of the group at byte
+ *                                   k/2, low nibble for even k. INT4 nibbles are sign-magnitude
+ *                                   (bit 3 sign, bits 0-2 |q|); MXFP4 nibbles are E2M1 codes.
+ *   wscale INT4: [G64][n_pad] bf16;  MXFP4: [B32][n_pad] E8M0 bytes (e + 127)
+ *   l1t    [rank_pad][K] bf16   : L1ᵀ, rows >= rank are zero
+ *   l2t    [n_pad][rank_pad] bf16 : L2ᵀ, columns >= rank are zero
+ *   xq, xscale : as wq, wscale with m_pad rows
+ *   xl1    [m_pad][rank_pad] fp32 : t = bf16(X̂)·L1 (fp32 accumulation)
+ * Returns W4A4_ERR_INVALID_ARG for M, N < 1, K not a positive multiple of 64, rank outside
+ * [0, min(N, K, W4A4_MAX_RANK)], or out == NULL; W4A4_ERR_UNSUPPORTED for an unknown fmt.
+ */
+w4a4_status_t w4a4_buffer_sizes(int M, int N, int K, int rank, int fmt, w4a4_sizes_t* out);
+
+/* ----------------------------------------------------------------- host (CPU, synchronous) */
+
+/*
+ * out[j] = max_i |A[i, j]| for a bf16 matrix A [rows][lda] (the activation / weight channel
+ * maxima the smoothing factor is built from, App. D). Thread-safe.
+ */
+w4a4_status_t w4a4_column_absmax(const uint16_t* A, int rows, int cols, int lda, float* out);
+
+/*
+ * Smoothing factors (App. D, after SmoothQuant): λ_j = max|X_j|^α / max|W_j|^(1-α).
+ * α = 0.5 is computed as fp32(sqrt(double(ax)/double(aw))); other α in (0, 1) as
+ * fp32(pow(ax, α) / pow(aw, 1 - α)) in double. λ_j = 1 when ax or aw is 0.
+ * inv_lambda[j] = 1.0f / λ_j (IEEE float division). W4A4_ERR_NUMERIC if a λ_j is not a
+ * finite normal float; W4A4_ERR_INVALID_ARG for α outside (0, 1) or negative maxima.
+ */
+w4a4_status_t w4a4_smooth_factors(const float* amax_x, const float* amax_w, int K, float alpha,
+                                  float* lambda, float* inv_lambda);
+
+/*
+ * Offline weight preparation (§4.2): Ŵ = W·diag(λ) (fp64); rank-r split Ŵᵀ ≈ L1·L2 with
+ * L1 = bf16(U_r Σ_r), L2 = bf16(V_rᵀ); residual R = fp32(Ŵ − (L1·L2)ᵀ) with the rank sum in
+ * fp64 in increasing rank order; R quantized per `fmt` into (wq, wscale); L1, L2 written
+ * transposed and zero-padded into (l1t, l2t).
+ *   W      [N][K] bf16 (host)
+ *   lambda [K] fp32 (host)
+ *   L1_in  [K][rank], L2_in [rank][N] bf16 (host) -- if both non-NULL they are used as the
+ *          factors (no SVD); if both NULL the library computes its own truncated SVD
+ *          (randomized subspace iteration + one-sided Jacobi; deterministic).
+ *   wq, wscale, l1t, l2t  host outputs sized by w4a4_buffer_sizes (copy them to the device).
+ *   L1_out [K][rank], L2_out [rank][N] bf16 (host, optional, may be NULL): the factors used.
+ * Thread-safe; uses several CPU threads.
+ */
+w4a4_status_t w4a4_prepare_weights(const uint16_t* W, int N, int K, const float* lambda, int rank,
+                                   int fmt, const uint16_t* L1_in, const uint16_t* L2_in,
+                                   uint8_t* wq, void* wscale, uint16_t* l1t, uint16_t* l2t,
+                                   uint16_t* L1_out, uint16_t* L2_out);
+
+/*
+ * LoRA merge without re-quantization (§2, §5.2: the low-rank branch absorbs a LoRA by growing
+ * its rank): L1' = [L1 | A], L2' = [L2 ; B], rank' = rank + ra. Reads the library-layout
+ * factors (l1t [rank_pad][K], l2t [n_pad][rank_pad]) and writes the merged ones
+ * (l1t_out [rank_pad'][K], l2t_out [n_pad][rank_pad']); A [K][ra], B [ra][N] bf16. Host
+ * buffers. The 4-bit codes and scales are not touched (they are not even passed in).
+ */
+w4a4_status_t w4a4_append_lowrank(const uint16_t* l1t, const uint16_t* l2t, int K, int N, int rank,
+                                  const uint16_t* A, const uint16_t* B, int ra,
+                                  uint16_t* l1t_out, uint16_t* l2t_out);
+
+/*
+ * Library code layout -> canonical: out [rows][K/2] bytes, code 2i in the low nibble; INT4
+ * codes become two's-complement nibbles, MXFP4 codes stay E2M1. `q` is a wq or xq buffer
+ * (host copy) with roundup(rows, 256) padded rows.
+ */
+w4a4_status_t w4a4_codes_to_canonical(const uint8_t* q, int rows, int K, int fmt, uint8_t* out);
+
+/* Library scale layout -> canonical: INT4 out [rows][K/64] bf16; MXFP4 out [rows][K/32] bytes. */
+w4a4_status_t w4a4_scales_to_canonical(const void* s, int rows, int K, int fmt, void* out);
+
+/* ----------------------------------------------------- device (asynchronous on `stream`) */
+
+/*
+ * Activation side, one pass over X (§4.3: the down projection shares the activations with the
+ * quantizer). Per row m and group:
+ *   X̂ = fp32(X · inv_lambda) (one fp32 multiply); codes and scales of X̂ per `fmt`
+ *   (INT4: s = bf16(max|X̂|/7), q = rint(X̂ · (1/s)); MXFP4: e = min{e : 6·2^e >= max|X̂|},
+ *   E2M1 round-half-even of X̂ / 2^e); t = bf16(X̂) · L1 accumulated in fp32.
+ *   X          [M][ldx] bf16 device, ldx >= K, ldx % 8 == 0
+ *   inv_lambda [K] fp32 device
+ *   l1t        [rank_pad][K] bf16 device (NULL allowed when rank == 0)
+ *   xq, xscale, xl1 device outputs in library layout (xl1 may be NULL when rank == 0).
+ *   All m_pad rows of xq/xscale/xl1 are written (padding rows as zeros).
+ */
+w4a4_status_t w4a4_quantize_act(const uint16_t* X, int M, int K, int ldx, const float* inv_lambda,
+                                const uint16_t* l1t, int rank, int fmt,
+                                uint8_t* xq, void* xscale, float* xl1, w4a4_stream_t stream);
+
+/*
+ * The fused 4-bit GEMM with the low-rank up projection in its epilogue (§4.3):
+ *   Y[m][n] = bf16( Σ_g s_x[m,g] s_w[n,g] Σ_{k∈g} q_x[m,k] q_w[n,k]      (INT4)
+ *                   or Σ_b 2^(e_x+e_w) Σ_{k∈b} val(c_x) val(c_w)          (MXFP4)
+ *                 + Σ_i bf16(t[m][i]) · L2[i][n]  + bias[n] )
+ *   xq, xscale, xl1  outputs of w4a4_quantize_act (device)
+ *   wq, wscale, l2t  outputs of w4a4_prepare_weights, copied to the device
+ *   bias   [N] bf16 device or NULL
+ *   Y      [M][ldy] bf16 device, ldy >= N. Only the M x N block is written.
+ */
+w4a4_status_t w4a4_lowrank_linear(const uint8_t* xq, const void* xscale, const float* xl1,
+                                  const uint8_t* wq, const void* wscale, const uint16_t* l2t,
+                                  const uint16_t* bias, uint16_t* Y, int ldy,
+                                  int M, int N, int K, int rank, int fmt, w4a4_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A4_H */

@@ -345,11 +345,20 @@ def exact_case(m=64, k=128, n=96, r=2, seed=3):
     w = resid + (l1 @ l2).T
     bits = lambda a: O.f32_to_bf16_bits(a.astype(np.float32))
     assert np.array_equal(O.bf16_bits_to_f32(bits(x)), x) and np.array_equal(O.bf16_bits_to_f32(bits(w)), w)
-    y = [[sum(Fraction(float(x[i, kk])) * Fraction(float(resid[j, kk])) for kk in range(k))
-          + sum(Fraction(float(x[i, sel[t]])) * Fraction(float(l2[t, j])) for t in range(r))
-          for j in range(n)] for i in range(m)]
+    # exact result in scaled integers: x*2^3, resid*2^6 and l2*2^3 are integers (int64 matmul is exact)
+    xi = (x * 8).astype(np.int64)
+    ri = (resid * 64).astype(np.int64)
+    li = (l2 * 8).astype(np.int64)
+    acc = xi @ ri.T + 8 * (xi[:, sel] @ li)
+    y = acc.astype(np.float64) / 512.0
+    assert np.all(np.abs(acc) < 2 ** 53)
+    # cross-check a few entries with rational arithmetic
+    for i, j in ((0, 0), (m - 1, n - 1), (m // 2, n // 3)):
+        fr = sum(Fraction(float(x[i, kk])) * Fraction(float(resid[j, kk])) for kk in range(k)) + \
+            sum(Fraction(float(x[i, sel[t]])) * Fraction(float(l2[t, j])) for t in range(r))
+        assert Fraction(float(y[i, j])) == fr
     return dict(x_bits=bits(x), w_bits=bits(w), l1=l1.astype(np.float32), l2=l2.astype(np.float32),
-                y_exact=np.array([[float(v) for v in row] for row in y]), rank=r)
+                y_exact=y, rank=r)
 
 
 def test_exact_case_end_to_end():

@@ -1,0 +1,544 @@
+// Device half of libw4a4 for gfx950 (CDNA4): the fused activation quantizer with the low-rank
+// down projection, and the 4-bit GEMMs with the low-rank up projection in the epilogue.
+//
+// Method: SVDQuant summary page (arXiv 2411.05007v4) §4.2 (smoothing, low-rank branch,
+// quantized residual), §4.3 / Fig. 6 (the down projection shares X̂ with the quantizer; the up
+// projection is added to the 4-bit GEMM), §3 and App. D (INT4 qmax 7, per-group-64 symmetric
+// quantization with 16-bit scales; FP4 E2M1 with qmax 6).
+//
+// MFMA use on gfx950:
+//  * INT4 x INT4 products run on the fp8 (E4M3) MFMA v_mfma_scale_f32_32x32x64_f8f6f4. A 4-bit
+//    code q (|q| <= 7) is carried as the E4M3 subnormal sign|0000|mag, whose value is q * 2^-9,
+//    so every product and every partial sum of one 64-wide group is exact in fp32 (the result
+//    is 2^-18 * Σ q_x q_w, |Σ| <= 3136). One 32x32x64 MFMA is exactly one group.
+//  * The per-group scale product s_x[m,g] * s_w[n,g] of a 32x32 tile is produced as an exact
+//    outer product by one bf16 MFMA (v_mfma_f32_32x32x16_bf16 with one non-zero k), so the
+//    group epilogue costs one fp32 FMA per output element.
+//  * FP4 (E2M1) codes with E8M0 block scales run on the same scaled MFMA with the block scales
+//    applied by the hardware.
+//  * The low-rank branch uses the bf16 MFMAs (16x16x32 for the down projection, 32x32x16 for the
+//    up projection, accumulating straight into the GEMM accumulators).
+
+#include <hip/hip_runtime.h>
+
+#include "w4a4_internal.h"
+
+using namespace w4a4;
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16f(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// float -> bf16 bits, nearest-even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ v8bf as_bf16x8(v4i v) { return __builtin_bit_cast(v8bf, v); }
+
+// Sign-magnitude INT4 nibbles (8 per dword) -> fp8 E4M3 subnormal carriers (4 per dword).
+// Even codes (low nibble of each byte) and odd codes (high nibble) go to separate dwords; A and B
+// operands use the same split, so each MFMA dot product still pairs equal k.
+__device__ __forceinline__ uint32_t fp8_even(uint32_t w) { return (w & 0x07070707u) | ((w << 4) & 0x80808080u); }
+__device__ __forceinline__ uint32_t fp8_odd(uint32_t w) { return ((w >> 4) & 0x07070707u) | (w & 0x80808080u); }
+
+// ===================================================================================
+// Kernel 1: activation side. One block = 16 rows x all of K; QA_WAVES waves split the groups.
+// Per row and group: X̂ = fp32(x * inv_lambda); codes + scales; t += bf16(X̂) · L1 (MFMA).
+// ===================================================================================
+constexpr int QA_WAVES = 8;
+constexpr int QA_ROWS = 16;
+
+template <int FMT, int NT>  // NT = rank_pad / 16 (0 when there is no low-rank branch)
+__global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
+    const uint16_t* __restrict__ X, int M, int K, int ldx, const float* __restrict__ inv_lambda,
+    const uint16_t* __restrict__ l1t, int m_pad, uint8_t* __restrict__ xq, void* __restrict__ xscale,
+    float* __restrict__ xl1) {
+  extern __shared__ float s_part[];  // [QA_WAVES][QA_ROWS][NT*16]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, kc = lane >> 4;
+  const int m = blockIdx.x * QA_ROWS + r;
+  const bool valid = m < M;
+  const int G = K / W4A4_GROUP;
+  v4f acc[NT > 0 ? NT : 1];
+#pragma unroll
+  for (int c = 0; c < (NT > 0 ? NT : 1); ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* xrow = X + (size_t)(valid ? m : 0) * ldx;
+  for (int g = wave; g < G; g += QA_WAVES) {
+    const int k0 = g * W4A4_GROUP + kc * 8;
+    float xh[2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 xv = valid ? *reinterpret_cast<const uint4*>(xrow + k0 + 32 * h) : make_uint4(0, 0, 0, 0);
+      const float4 i0 = *reinterpret_cast<const float4*>(inv_lambda + k0 + 32 * h);
+      const float4 i1 = *reinterpret_cast<const float4*>(inv_lambda + k0 + 32 * h + 4);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      const float il[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1) ? (xw[e >> 1] >> 16) : (xw[e >> 1] & 0xFFFFu);
+        xh[h][e] = bf16f(bits) * il[e];  // one fp32 multiply (no contraction: nothing to fuse)
+      }
+    }
+    uint8_t* qdst = xq + ((size_t)g * m_pad + blockIdx.x * QA_ROWS + r) * 32 + kc * 4;
+    if (FMT == W4A4_FMT_INT4_G64) {
+      float amax = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xh[h][e]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      float s = bf16f(bf16_rne(amax / 7.0f));
+      if (!(s >= 0x1p-126f)) s = 0.f;
+      const float inv = s != 0.f ? 1.0f / s : 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float y = __builtin_rintf(xh[h][e] * inv);
+          y = fminf(7.f, fmaxf(-7.f, y));
+          const int q = (int)y;
+          const uint32_t nib = (q < 0 ? 8u : 0u) | (uint32_t)(q < 0 ? -q : q);
+          word |= nib << (4 * e);
+        }
+        *reinterpret_cast<uint32_t*>(qdst + 16 * h) = word;
+      }
+      if (kc == 0) static_cast<uint16_t*>(xscale)[(size_t)g * m_pad + blockIdx.x * QA_ROWS + r] = (uint16_t)bf16_rne(s);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xh[h][e]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        int ex;
+        int e8;
+        if (amax == 0.f) {
+          e8 = -127;
+        } else {
+          const float mant = frexpf(amax, &ex);  // amax = mant * 2^ex, mant in [0.5, 1)
+          e8 = mant <= 0.75f ? ex - 3 : ex - 2;
+          e8 = max(-127, min(127, e8));
+        }
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = ldexpf(xh[h][e], -e8);
+          const float a = fabsf(y);
+          const uint32_t idx = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+          const uint32_t nib = ((__float_as_uint(y) >> 28) & 8u) | idx;
+          word |= nib << (4 * e);
+        }
+        *reinterpret_cast<uint32_t*>(qdst + 16 * h) = word;
+        if (kc == 0)
+          static_cast<uint8_t*>(xscale)[(size_t)(2 * g + h) * m_pad + blockIdx.x * QA_ROWS + r] = (uint8_t)(e8 + 127);
+      }
+    }
+    if (NT > 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v4i a;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) a[d] = (int)(bf16_rne(xh[h][2 * d]) | (bf16_rne(xh[h][2 * d + 1]) << 16));
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const v4i b = *reinterpret_cast<const v4i*>(l1t + (size_t)(c * 16 + r) * K + k0 + 32 * h);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc[c], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (NT > 0) {
+    constexpr int RP = NT * 16;
+    // 16x16 MFMA output: lane holds column lane%16, rows 4*(lane/16) + v
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_part[(wave * QA_ROWS + 4 * kc + v) * RP + c * 16 + r] = acc[c][v];
+    __syncthreads();
+    for (int i = threadIdx.x; i < QA_ROWS * RP; i += QA_WAVES * 64) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < QA_WAVES; ++w) t += s_part[w * QA_ROWS * RP + i];
+      xl1[(size_t)blockIdx.x * QA_ROWS * RP + i] = t;
+    }
+  }
+}
+
+// ===================================================================================
+// Kernel 2: INT4 GEMM + group-scale epilogue + low-rank up projection (+ bias), bf16 out.
+// Block tile BM x BN, 2 x 2 waves, each wave a 2 x 2 grid of 32x32 tiles. One K step = one
+// 64-wide group, double-buffered in LDS. Codes are converted to fp8 once per block while being
+// staged into LDS; scales are staged alongside.
+// ===================================================================================
+constexpr int GB_M = 128, GB_N = 128, G_THREADS = 256;
+
+// LDS chunk swizzle: row r, 16-byte chunk c (0..3) of a 64-byte fp8 row
+__device__ __forceinline__ int sw_off64(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+
+template <int NTR>  // NTR = rank_pad / 16
+__global__ __launch_bounds__(G_THREADS) void gemm_int4_kernel(
+    const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs, const float* __restrict__ xl1,
+    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
+    int m_pad, int n_pad) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][GB_M * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][GB_N * 64];
+  __shared__ uint16_t s_sa[2][GB_M];
+  __shared__ uint16_t s_sb[2][GB_N];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = m_pad / GB_M;
+  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  const int m0 = tm * GB_M, n0 = tn * GB_N;
+  const int G = K / W4A4_GROUP;
+
+  // global -> register staging: thread loads 16 B of A and 16 B of B (row tid/2, half tid%2)
+  const int lrow = tid >> 1, lhalf = tid & 1;
+  const uint8_t* a_src = xq + ((size_t)(m0 + lrow)) * 32 + lhalf * 16;
+  const uint8_t* b_src = wq + ((size_t)(n0 + lrow)) * 32 + lhalf * 16;
+  const size_t a_gstride = (size_t)m_pad * 32, b_gstride = (size_t)n_pad * 32;
+
+  uint4 ra, rb;
+  uint32_t rs = 0;
+  auto gload = [&](int g) {
+    ra = *reinterpret_cast<const uint4*>(a_src + g * a_gstride);
+    rb = *reinterpret_cast<const uint4*>(b_src + g * b_gstride);
+    if (tid < 64) rs = *reinterpret_cast<const uint32_t*>(xs + (size_t)g * m_pad + m0 + 2 * tid);
+    else if (tid < 128) rs = *reinterpret_cast<const uint32_t*>(ws + (size_t)g * n_pad + n0 + 2 * (tid - 64));
+  };
+  auto lstore = [&](int buf) {
+    const uint32_t aw[4] = {ra.x, ra.y, ra.z, ra.w}, bw[4] = {rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint4 fa = make_uint4(fp8_even(aw[2 * j]), fp8_odd(aw[2 * j]), fp8_even(aw[2 * j + 1]), fp8_odd(aw[2 * j + 1]));
+      uint4 fb = make_uint4(fp8_even(bw[2 * j]), fp8_odd(bw[2 * j]), fp8_even(bw[2 * j + 1]), fp8_odd(bw[2 * j + 1]));
+      *reinterpret_cast<uint4*>(&s_a[buf][sw_off64(lrow, 2 * lhalf + j)]) = fa;
+      *reinterpret_cast<uint4*>(&s_b[buf][sw_off64(lrow, 2 * lhalf + j)]) = fb;
+    }
+    if (tid < 64) *reinterpret_cast<uint32_t*>(&s_sa[buf][2 * tid]) = rs;
+    else if (tid < 128) *reinterpret_cast<uint32_t*>(&s_sb[buf][2 * (tid - 64)]) = rs;
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const v16f zero16 = {};
+  const int lr = lane & 31, lh = lane >> 5;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const int buf = g & 1;
+    if (g + 1 < G) gload(g + 1);
+    v8i A[2], B[2];
+    v4i OA[2], OB[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = wm * 64 + i * 32 + lr;
+      const v4i lo = *reinterpret_cast<const v4i*>(&s_a[buf][sw_off64(row, 2 * lh)]);
+      const v4i hi = *reinterpret_cast<const v4i*>(&s_a[buf][sw_off64(row, 2 * lh + 1)]);
+      A[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      // exact outer-product operand: bf16(s_x * 2^9) at k = 0 (lanes 0..31), zero elsewhere
+      const uint32_t sx = lh == 0 ? bf16_rne(bf16f(s_sa[buf][wm * 64 + i * 32 + lr]) * 512.f) : 0u;
+      OA[i] = v4i{(int)sx, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = wn * 64 + j * 32 + lr;
+      const v4i lo = *reinterpret_cast<const v4i*>(&s_b[buf][sw_off64(col, 2 * lh)]);
+      const v4i hi = *reinterpret_cast<const v4i*>(&s_b[buf][sw_off64(col, 2 * lh + 1)]);
+      B[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const uint32_t sw = lh == 0 ? bf16_rne(bf16f(s_sb[buf][wn * 64 + j * 32 + lr]) * 512.f) : 0u;
+      OB[j] = v4i{(int)sw, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[i], B[j], zero16, 0, 0, 0, 127, 0, 127);
+        const v16f s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(OA[i]), as_bf16x8(OB[j]), zero16, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], s[v], acc[i][j][v]);
+      }
+    if (g + 1 < G) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // low-rank up projection: acc += bf16(t) · L2 over k = rank index (32x32x16 bf16 MFMA)
+  if (NTR > 0) {
+    constexpr int RP = NTR * 16;
+#pragma unroll
+    for (int kk = 0; kk < RP; kk += 16) {
+      v4i TA[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float* tp = xl1 + (size_t)(m0 + wm * 64 + i * 32 + lr) * RP + kk + 8 * lh;
+        const float4 t0 = *reinterpret_cast<const float4*>(tp);
+        const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
+        TA[i] = v4i{(int)(bf16_rne(t0.x) | (bf16_rne(t0.y) << 16)), (int)(bf16_rne(t0.z) | (bf16_rne(t0.w) << 16)),
+                    (int)(bf16_rne(t1.x) | (bf16_rne(t1.y) << 16)), (int)(bf16_rne(t1.z) | (bf16_rne(t1.w) << 16))};
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const v4i lb = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 64 + j * 32 + lr) * RP + kk + 8 * lh);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(TA[i]), as_bf16x8(lb), acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // store: 32x32 output layout, lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + wn * 64 + j * 32 + lr;
+    if (col >= N) continue;
+    const float bcol = bias ? bf16f(bias[col]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+        if (row < M) Y[(size_t)row * ldy + col] = (uint16_t)bf16_rne(acc[i][j][v] + bcol);
+      }
+  }
+}
+
+// ===================================================================================
+// Kernel 3: MXFP4 GEMM (E2M1 x E2M1 with E8M0 block scales applied by the MFMA) + low-rank
+// epilogue. Same tiling as kernel 2; one K step = 64 = two 32-blocks (lanes 0-31 / 32-63).
+// ===================================================================================
+__device__ __forceinline__ int sw_off32(int r, int h) { return r * 32 + 16 * (h ^ ((r >> 3) & 1)); }
+
+template <int NTR>
+__global__ __launch_bounds__(G_THREADS) void gemm_mxfp4_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ xl1,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
+    int m_pad, int n_pad) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][GB_M * 32];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][GB_N * 32];
+  __shared__ uint8_t s_sa[2][2][GB_M];
+  __shared__ uint8_t s_sb[2][2][GB_N];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = m_pad / GB_M;
+  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  const int m0 = tm * GB_M, n0 = tn * GB_N;
+  const int G = K / W4A4_GROUP;
+
+  const int lrow = tid >> 1, lhalf = tid & 1;
+  const uint8_t* a_src = xq + ((size_t)(m0 + lrow)) * 32 + lhalf * 16;
+  const uint8_t* b_src = wq + ((size_t)(n0 + lrow)) * 32 + lhalf * 16;
+  const size_t a_gstride = (size_t)m_pad * 32, b_gstride = (size_t)n_pad * 32;
+
+  uint4 ra, rb;
+  uint32_t rs = 0;
+  // scales: 2 blocks x 128 rows = 256 bytes per operand; threads 0..63 -> A, 64..127 -> B (4 B each)
+  auto gload = [&](int g) {
+    ra = *reinterpret_cast<const uint4*>(a_src + g * a_gstride);
+    rb = *reinterpret_cast<const uint4*>(b_src + g * b_gstride);
+    if (tid < 64) {
+      const int blk = tid >> 5, rr = (tid & 31) * 4;
+      rs = *reinterpret_cast<const uint32_t*>(xs + (size_t)(2 * g + blk) * m_pad + m0 + rr);
+    } else if (tid < 128) {
+      const int t2 = tid - 64, blk = t2 >> 5, rr = (t2 & 31) * 4;
+      rs = *reinterpret_cast<const uint32_t*>(ws + (size_t)(2 * g + blk) * n_pad + n0 + rr);
+    }
+  };
+  auto lstore = [&](int buf) {
+    *reinterpret_cast<uint4*>(&s_a[buf][sw_off32(lrow, lhalf)]) = ra;
+    *reinterpret_cast<uint4*>(&s_b[buf][sw_off32(lrow, lhalf)]) = rb;
+    if (tid < 64) *reinterpret_cast<uint32_t*>(&s_sa[buf][tid >> 5][(tid & 31) * 4]) = rs;
+    else if (tid < 128) *reinterpret_cast<uint32_t*>(&s_sb[buf][(tid - 64) >> 5][((tid - 64) & 31) * 4]) = rs;
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const int buf = g & 1;
+    if (g + 1 < G) gload(g + 1);
+    v8i A[2], B[2];
+    int SA[2], SB[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = wm * 64 + i * 32 + lr;
+      const v4i v = *reinterpret_cast<const v4i*>(&s_a[buf][sw_off32(row, lh)]);
+      A[i] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+      SA[i] = s_sa[buf][lh][row];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = wn * 64 + j * 32 + lr;
+      const v4i v = *reinterpret_cast<const v4i*>(&s_b[buf][sw_off32(col, lh)]);
+      B[j] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+      SB[j] = s_sb[buf][lh][col];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[i], B[j], acc[i][j], 4, 4, 0, SA[i], 0, SB[j]);
+    if (g + 1 < G) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (NTR > 0) {
+    constexpr int RP = NTR * 16;
+#pragma unroll
+    for (int kk = 0; kk < RP; kk += 16) {
+      v4i TA[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float* tp = xl1 + (size_t)(m0 + wm * 64 + i * 32 + lr) * RP + kk + 8 * lh;
+        const float4 t0 = *reinterpret_cast<const float4*>(tp);
+        const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
+        TA[i] = v4i{(int)(bf16_rne(t0.x) | (bf16_rne(t0.y) << 16)), (int)(bf16_rne(t0.z) | (bf16_rne(t0.w) << 16)),
+                    (int)(bf16_rne(t1.x) | (bf16_rne(t1.y) << 16)), (int)(bf16_rne(t1.z) | (bf16_rne(t1.w) << 16))};
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const v4i lb = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 64 + j * 32 + lr) * RP + kk + 8 * lh);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(TA[i]), as_bf16x8(lb), acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + wn * 64 + j * 32 + lr;
+    if (col >= N) continue;
+    const float bcol = bias ? bf16f(bias[col]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+        if (row < M) Y[(size_t)row * ldy + col] = (uint16_t)bf16_rne(acc[i][j][v] + bcol);
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------- launch helpers
+template <int FMT, int NT>
+hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, const uint16_t* l1t, int m_pad,
+                     uint8_t* xq, void* xs, float* xl1, hipStream_t st) {
+  const size_t lds = NT > 0 ? sizeof(float) * QA_WAVES * QA_ROWS * NT * 16 : 0;
+  hipLaunchKernelGGL((quantize_act_kernel<FMT, NT>), dim3(m_pad / QA_ROWS), dim3(QA_WAVES * 64), lds, st, X, M, K,
+                     ldx, il, l1t, m_pad, xq, xs, xl1);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t dispatch_qa(int nt, const uint16_t* X, int M, int K, int ldx, const float* il, const uint16_t* l1t,
+                       int m_pad, uint8_t* xq, void* xs, float* xl1, hipStream_t st) {
+  switch (nt) {
+#define W4A4_QA_CASE(n) \
+  case n: return launch_qa<FMT, n>(X, M, K, ldx, il, l1t, m_pad, xq, xs, xl1, st);
+    W4A4_QA_CASE(0) W4A4_QA_CASE(1) W4A4_QA_CASE(2) W4A4_QA_CASE(3) W4A4_QA_CASE(4)
+    W4A4_QA_CASE(5) W4A4_QA_CASE(6) W4A4_QA_CASE(7) W4A4_QA_CASE(8)
+#undef W4A4_QA_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int NTR>
+hipError_t launch_gemm(int fmt, const uint8_t* xq, const void* xs, const float* xl1, const uint8_t* wq,
+                       const void* ws, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy, int M,
+                       int N, int K, int m_pad, int n_pad, hipStream_t st) {
+  const dim3 grid((m_pad / GB_M) * (n_pad / GB_N));
+  if (fmt == W4A4_FMT_INT4_G64)
+    hipLaunchKernelGGL((gemm_int4_kernel<NTR>), grid, dim3(G_THREADS), 0, st, xq, static_cast<const uint16_t*>(xs),
+                       xl1, wq, static_cast<const uint16_t*>(ws), l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
+  else
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<NTR>), grid, dim3(G_THREADS), 0, st, xq, static_cast<const uint8_t*>(xs),
+                       xl1, wq, static_cast<const uint8_t*>(ws), l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_gemm(int ntr, int fmt, const uint8_t* xq, const void* xs, const float* xl1, const uint8_t* wq,
+                         const void* ws, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy, int M,
+                         int N, int K, int m_pad, int n_pad, hipStream_t st) {
+  switch (ntr) {
+#define W4A4_G_CASE(n) \
+  case n: return launch_gemm<n>(fmt, xq, xs, xl1, wq, ws, l2t, bias, Y, ldy, M, N, K, m_pad, n_pad, st);
+    W4A4_G_CASE(0) W4A4_G_CASE(1) W4A4_G_CASE(2) W4A4_G_CASE(3) W4A4_G_CASE(4)
+    W4A4_G_CASE(5) W4A4_G_CASE(6) W4A4_G_CASE(7) W4A4_G_CASE(8)
+#undef W4A4_G_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// ================================================================================ C ABI (device)
+extern "C" {
+
+w4a4_status_t w4a4_quantize_act(const uint16_t* X, int M, int K, int ldx, const float* inv_lambda,
+                                const uint16_t* l1t, int rank, int fmt, uint8_t* xq, void* xscale, float* xl1,
+                                w4a4_stream_t stream) {
+  if (!fmt_known(fmt)) return W4A4_ERR_UNSUPPORTED;
+  // N is not involved on this side; rank <= K is the relevant bound
+  w4a4_status_t st = check_shape(M, rank > 0 ? rank : 1, K, rank, fmt);
+  if (st != W4A4_OK) return st;
+  if (!X || !inv_lambda || !xq || !xscale) return W4A4_ERR_INVALID_ARG;
+  if (ldx < K || ldx % 8 != 0) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(inv_lambda) || !aligned16(xq) || !aligned16(xscale)) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!l1t || !xl1 || !aligned16(l1t) || !aligned16(xl1))) return W4A4_ERR_INVALID_ARG;
+  const int m_pad = rows_pad_of(M), nt = rank_pad_of(rank) / 16;
+  hipError_t e = fmt == W4A4_FMT_INT4_G64
+                     ? dispatch_qa<W4A4_FMT_INT4_G64>(nt, X, M, K, ldx, inv_lambda, l1t, m_pad, xq, xscale, xl1,
+                                                      reinterpret_cast<hipStream_t>(stream))
+                     : dispatch_qa<W4A4_FMT_MXFP4_B32>(nt, X, M, K, ldx, inv_lambda, l1t, m_pad, xq, xscale, xl1,
+                                                       reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP;
+}
+
+w4a4_status_t w4a4_lowrank_linear(const uint8_t* xq, const void* xscale, const float* xl1, const uint8_t* wq,
+                                  const void* wscale, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y,
+                                  int ldy, int M, int N, int K, int rank, int fmt, w4a4_stream_t stream) {
+  w4a4_status_t st = check_shape(M, N, K, rank, fmt);
+  if (st != W4A4_OK) return st;
+  if (!xq || !xscale || !wq || !wscale || !Y || ldy < N) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(xscale) || !aligned16(wq) || !aligned16(wscale)) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!xl1 || !l2t || !aligned16(xl1) || !aligned16(l2t))) return W4A4_ERR_INVALID_ARG;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return W4A4_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(Y) & 1u) return W4A4_ERR_INVALID_ARG;
+  hipError_t e = dispatch_gemm(rank_pad_of(rank) / 16, fmt, xq, xscale, xl1, wq, wscale, l2t, bias, Y, ldy, M, N, K,
+                               rows_pad_of(M), rows_pad_of(N), reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,511 @@
+// Host half of libw4a4: smoothing factors, the rank-r split (own truncated SVD), residual
+// quantization, library layouts and their canonical forms.
+//
+// Method: SVDQuant summary page (arXiv 2411.05007v4) §4.2 / Fig. 4 (smoothing, SVD low-rank
+// branch, quantized residual), §3 (qmax of signed INT4 and of E2M1 FP4), App. D (per-group-64
+// symmetric INT4 with 16-bit scales; smoothing from activation and weight maxima).
+//
+// Everything here is deterministic and bit-reproducible: each fp32/fp64 step is an IEEE
+// operation in a fixed order (built with -ffp-contract=off, no fast-math).
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <functional>
+#include <new>
+#include <thread>
+#include <vector>
+
+#include "w4a4_internal.h"
+
+using namespace w4a4;
+
+namespace {
+
+// ------------------------------------------------------------------------------ helpers
+inline float bf16_to_f32(uint16_t h) {
+  uint32_t u = uint32_t(h) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// float -> bf16 bits, round to nearest, ties to even (finite inputs)
+inline uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+inline float bf16_round(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+int worker_count() {
+  unsigned h = std::thread::hardware_concurrency();
+  return int(std::max(1u, std::min(h, 16u)));
+}
+
+// Run fn(begin, end, worker) over [0, n) split into contiguous chunks, one per worker.
+void parallel_for(int n, const std::function<void(int, int, int)>& fn) {
+  int nw = std::min(worker_count(), std::max(1, n));
+  if (nw == 1) {
+    fn(0, n, 0);
+    return;
+  }
+  std::vector<std::thread> ts;
+  int chunk = (n + nw - 1) / nw;
+  for (int w = 0; w < nw; ++w) {
+    int b = w * chunk, e = std::min(n, b + chunk);
+    if (b >= e) break;
+    ts.emplace_back(fn, b, e, w);
+  }
+  for (auto& t : ts) t.join();
+}
+
+// ------------------------------------------------------------------------------ quantizers
+// One INT4 group (64 values): s = bf16(max|v| / 7); q = clamp(rint(v * (1/s))); a scale below
+// 2^-126 is stored as 0 with zero codes. Symmetric scaling bounds |v * (1/s)| by
+// 7 / (1 - 2^-8) * (1 + 2^-23)^2 < 7.5, so |q| <= 7 and the sign-magnitude nibble is exact.
+void quant_int4_group(const float* v, uint8_t* out32, uint16_t* scale_bits) {
+  float amax = 0.0f;
+  for (int k = 0; k < W4A4_GROUP; ++k) amax = std::max(amax, std::fabs(v[k]));
+  float s = bf16_round(amax / 7.0f);
+  if (!(s >= 0x1p-126f)) s = 0.0f;
+  *scale_bits = f32_to_bf16(s);
+  uint8_t nib[W4A4_GROUP] = {};
+  if (s != 0.0f) {
+    const float inv = 1.0f / s;
+    for (int k = 0; k < W4A4_GROUP; ++k) {
+      float y = v[k] * inv;
+      int q = int(std::nearbyint(y));
+      q = std::min(7, std::max(-7, q));
+      nib[k] = uint8_t((q < 0 ? 8 : 0) | (q < 0 ? -q : q));
+    }
+  }
+  for (int i = 0; i < W4A4_GROUP / 2; ++i) out32[i] = uint8_t(nib[2 * i] | (nib[2 * i + 1] << 4));
+}
+
+// e = the smallest integer with 6 * 2^e >= amax, in [-127, 127]; -127 for amax == 0.
+int mx_exponent(float amax) {
+  if (amax == 0.0f) return -127;
+  int ex;
+  double m = std::frexp(double(amax), &ex);  // amax = m * 2^ex, m in [0.5, 1)
+  int e = (m <= 0.75) ? ex - 3 : ex - 2;
+  return std::min(127, std::max(-127, e));
+}
+
+// E2M1 code of y (|y| <= 6 by construction): nearest of 0,.5,1,1.5,2,3,4,6, ties to the even
+// code; bit 3 is the sign bit of y (kept for magnitudes that round to 0).
+uint8_t e2m1_code(double y) {
+  double a = std::fabs(y);
+  int idx = a <= 0.25 ? 0 : a < 0.75 ? 1 : a <= 1.25 ? 2 : a < 1.75 ? 3
+          : a <= 2.5 ? 4 : a < 3.5 ? 5 : a <= 5.0 ? 6 : 7;
+  return uint8_t((std::signbit(y) ? 8 : 0) | idx);
+}
+
+// One MXFP4 64-wide chunk (two blocks of 32): codes packed like the INT4 chunk, two E8M0 bytes.
+void quant_mxfp4_chunk(const float* v, uint8_t* out32, uint8_t* e8_lo, uint8_t* e8_hi) {
+  uint8_t nib[W4A4_GROUP];
+  for (int b = 0; b < 2; ++b) {
+    const float* vb = v + b * W4A4_MX_BLOCK;
+    float amax = 0.0f;
+    for (int k = 0; k < W4A4_MX_BLOCK; ++k) amax = std::max(amax, std::fabs(vb[k]));
+    int e = mx_exponent(amax);
+    (b ? *e8_hi : *e8_lo) = uint8_t(e + 127);
+    for (int k = 0; k < W4A4_MX_BLOCK; ++k) nib[b * W4A4_MX_BLOCK + k] = e2m1_code(std::ldexp(double(vb[k]), -e));
+  }
+  for (int i = 0; i < W4A4_GROUP / 2; ++i) out32[i] = uint8_t(nib[2 * i] | (nib[2 * i + 1] << 4));
+}
+
+// ------------------------------------------------------------------------------ own SVD
+// Truncated SVD of Ŵᵀ (Ŵ is [N][K] row-major, fp64) by randomized subspace iteration
+// (Halko, Martinsson & Tropp 2011, Alg. 4.4) followed by a one-sided Jacobi SVD (Hestenes) of
+// the small projected matrix. Outputs: u [r][K] (left vectors of Ŵᵀ), sigma [r], v [r][N].
+
+uint64_t splitmix64(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+double gaussian(uint64_t& s) {  // Box-Muller on two uniforms in (0, 1)
+  double u1 = (double((splitmix64(s) >> 11)) + 0.5) * 0x1p-53;
+  double u2 = (double((splitmix64(s) >> 11)) + 0.5) * 0x1p-53;
+  return std::sqrt(-2.0 * std::log(u1)) * std::cos(6.283185307179586 * u2);
+}
+
+// Y[j][n] = Σ_k W[n][k] Z[j][k]   (W [N][K], Z [l][K], Y [l][N]; column-major panels)
+void mul_w(const double* W, int N, int K, const double* Z, int l, double* Y) {
+  parallel_for(N, [&](int b, int e, int) {
+    for (int n = b; n < e; ++n) {
+      const double* w = W + size_t(n) * K;
+      for (int j = 0; j < l; ++j) {
+        const double* z = Z + size_t(j) * K;
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k) acc += w[k] * z[k];
+        Y[size_t(j) * N + n] = acc;
+      }
+    }
+  });
+}
+
+// Z[j][k] = Σ_n W[n][k] Y[j][n]   (per-worker partial sums reduced in worker order)
+void mul_wt(const double* W, int N, int K, const double* Y, int l, double* Z) {
+  int nw = std::min(worker_count(), N);
+  std::vector<std::vector<double>> part(nw, std::vector<double>(size_t(l) * K, 0.0));
+  parallel_for(N, [&](int b, int e, int w) {
+    double* zp = part[w].data();
+    for (int n = b; n < e; ++n) {
+      const double* wr = W + size_t(n) * K;
+      for (int j = 0; j < l; ++j) {
+        const double c = Y[size_t(j) * N + n];
+        double* z = zp + size_t(j) * K;
+        for (int k = 0; k < K; ++k) z[k] += c * wr[k];
+      }
+    }
+  });
+  std::fill(Z, Z + size_t(l) * K, 0.0);
+  for (int w = 0; w < nw; ++w)
+    for (size_t i = 0; i < size_t(l) * K; ++i) Z[i] += part[w][i];
+}
+
+// Orthonormalize the l columns (each of length n, stored contiguously) by modified Gram-Schmidt,
+// twice. Columns that vanish become zero.
+void orthonormalize(double* Q, int n, int l) {
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int j = 0; j < l; ++j) {
+      double* qj = Q + size_t(j) * n;
+      for (int i = 0; i < j; ++i) {
+        const double* qi = Q + size_t(i) * n;
+        double d = 0.0;
+        for (int t = 0; t < n; ++t) d += qi[t] * qj[t];
+        for (int t = 0; t < n; ++t) qj[t] -= d * qi[t];
+      }
+      double nrm = 0.0;
+      for (int t = 0; t < n; ++t) nrm += qj[t] * qj[t];
+      nrm = std::sqrt(nrm);
+      if (nrm > 1e-300) {
+        for (int t = 0; t < n; ++t) qj[t] /= nrm;
+      } else {
+        std::fill(qj, qj + n, 0.0);
+      }
+    }
+  }
+}
+
+// One-sided Jacobi on the l columns of Z (length K each): Z J = U Σ. Returns false if it did not
+// converge. On exit Z holds U Σ (orthogonal columns) and J [l][l] (J[i][j] = row i, col j).
+bool jacobi_svd(double* Z, int K, int l, double* J) {
+  for (int i = 0; i < l; ++i)
+    for (int j = 0; j < l; ++j) J[size_t(i) * l + j] = (i == j) ? 1.0 : 0.0;
+  for (int sweep = 0; sweep < 60; ++sweep) {
+    bool rotated = false;
+    for (int p = 0; p < l - 1; ++p) {
+      for (int q = p + 1; q < l; ++q) {
+        double* zp = Z + size_t(p) * K;
+        double* zq = Z + size_t(q) * K;
+        double a = 0.0, b = 0.0, g = 0.0;
+        for (int k = 0; k < K; ++k) {
+          a += zp[k] * zp[k];
+          b += zq[k] * zq[k];
+          g += zp[k] * zq[k];
+        }
+        if (a == 0.0 || b == 0.0 || std::fabs(g) <= 1e-15 * std::sqrt(a * b)) continue;
+        rotated = true;
+        double zeta = (b - a) / (2.0 * g);
+        double t = (zeta >= 0 ? 1.0 : -1.0) / (std::fabs(zeta) + std::sqrt(1.0 + zeta * zeta));
+        double c = 1.0 / std::sqrt(1.0 + t * t), s = c * t;
+        for (int k = 0; k < K; ++k) {
+          double x = zp[k], y = zq[k];
+          zp[k] = c * x - s * y;
+          zq[k] = s * x + c * y;
+        }
+        for (int i = 0; i < l; ++i) {
+          double x = J[size_t(i) * l + p], y = J[size_t(i) * l + q];
+          J[size_t(i) * l + p] = c * x - s * y;
+          J[size_t(i) * l + q] = s * x + c * y;
+        }
+      }
+    }
+    if (!rotated) return true;
+  }
+  return false;
+}
+
+// Top-r singular triplets of Ŵᵀ. u: [r][K], v: [r][N]. Deterministic (fixed seed).
+bool truncated_svd(const double* W, int N, int K, int r, std::vector<double>& u,
+                   std::vector<double>& sigma, std::vector<double>& v) {
+  const int mn = std::min(N, K);
+  const int l = std::min(mn, 2 * r + 16);  // oversampling: the bulk of Ŵ's spectrum has small gaps
+  const int iters = 12;
+  std::vector<double> Z(size_t(l) * K), Y(size_t(l) * N), J(size_t(l) * l);
+  uint64_t seed = 0x5EEDC0DE12345678ull;
+  for (auto& z : Z) z = gaussian(seed);
+  mul_w(W, N, K, Z.data(), l, Y.data());  // Y = Ŵ Ω
+  orthonormalize(Y.data(), N, l);
+  for (int it = 0; it < iters; ++it) {
+    mul_wt(W, N, K, Y.data(), l, Z.data());  // Z = Ŵᵀ Y
+    orthonormalize(Z.data(), K, l);
+    mul_w(W, N, K, Z.data(), l, Y.data());   // Y = Ŵ Z
+    orthonormalize(Y.data(), N, l);
+  }
+  mul_wt(W, N, K, Y.data(), l, Z.data());    // Z = Ŵᵀ Y = (Yᵀ Ŵ)ᵀ, K x l
+  if (!jacobi_svd(Z.data(), K, l, J.data())) return false;
+  std::vector<double> nrm(l);
+  std::vector<int> order(l);
+  for (int j = 0; j < l; ++j) {
+    double s = 0.0;
+    const double* z = Z.data() + size_t(j) * K;
+    for (int k = 0; k < K; ++k) s += z[k] * z[k];
+    nrm[j] = std::sqrt(s);
+    order[j] = j;
+  }
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return nrm[a] > nrm[b]; });
+  u.assign(size_t(r) * K, 0.0);
+  v.assign(size_t(r) * N, 0.0);
+  sigma.assign(r, 0.0);
+  for (int i = 0; i < r; ++i) {
+    const int j = order[i];
+    sigma[i] = nrm[j];
+    const double* z = Z.data() + size_t(j) * K;
+    double* ui = u.data() + size_t(i) * K;
+    if (nrm[j] > 0) {
+      for (int k = 0; k < K; ++k) ui[k] = z[k] / nrm[j];
+    }
+    double* vi = v.data() + size_t(i) * N;  // right vectors: Y J[:, j]
+    for (int t = 0; t < l; ++t) {
+      const double c = J[size_t(t) * l + j];
+      const double* yt = Y.data() + size_t(t) * N;
+      for (int n = 0; n < N; ++n) vi[n] += c * yt[n];
+    }
+    // sign: the largest-magnitude entry of the left vector is positive (ties: lowest index)
+    int lead = 0;
+    for (int k = 1; k < K; ++k)
+      if (std::fabs(ui[k]) > std::fabs(ui[lead])) lead = k;
+    if (ui[lead] < 0) {
+      for (int k = 0; k < K; ++k) ui[k] = -ui[k];
+      for (int n = 0; n < N; ++n) vi[n] = -vi[n];
+    }
+  }
+  return true;
+}
+
+}  // namespace
+
+// ================================================================================ C ABI (host)
+extern "C" {
+
+int w4a4_abi_version(void) { return W4A4_ABI_VERSION; }
+
+const char* w4a4_status_str(w4a4_status_t s) {
+  switch (s) {
+    case W4A4_OK: return "ok";
+    case W4A4_ERR_INVALID_ARG: return "invalid argument";
+    case W4A4_ERR_UNSUPPORTED: return "unsupported format";
+    case W4A4_ERR_NUMERIC: return "numeric error";
+    case W4A4_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+w4a4_status_t w4a4_buffer_sizes(int M, int N, int K, int rank, int fmt, w4a4_sizes_t* out) {
+  if (!out) return W4A4_ERR_INVALID_ARG;
+  w4a4_status_t st = check_shape(M, N, K, rank, fmt);
+  if (st != W4A4_OK) return st;
+  const size_t mp = size_t(rows_pad_of(M)), np = size_t(rows_pad_of(N)), rp = size_t(rank_pad_of(rank));
+  const size_t kk = size_t(K);
+  const bool mx = fmt == W4A4_FMT_MXFP4_B32;
+  out->m_pad = int(mp);
+  out->n_pad = int(np);
+  out->rank_pad = int(rp);
+  out->wq = np * kk / 2;
+  out->wscale = mx ? (kk / W4A4_MX_BLOCK) * np : (kk / W4A4_GROUP) * np * 2;
+  out->l1t = rp * kk * 2;
+  out->l2t = np * rp * 2;
+  out->xq = mp * kk / 2;
+  out->xscale = mx ? (kk / W4A4_MX_BLOCK) * mp : (kk / W4A4_GROUP) * mp * 2;
+  out->xl1 = mp * rp * 4;
+  return W4A4_OK;
+}
+
+w4a4_status_t w4a4_column_absmax(const uint16_t* A, int rows, int cols, int lda, float* out) {
+  if (!A || !out || rows < 1 || cols < 1 || lda < cols) return W4A4_ERR_INVALID_ARG;
+  std::vector<float> acc(static_cast<size_t>(cols), 0.0f);
+  for (int i = 0; i < rows; ++i) {
+    const uint16_t* a = A + size_t(i) * lda;
+    for (int j = 0; j < cols; ++j) acc[j] = std::max(acc[j], std::fabs(bf16_to_f32(a[j])));
+  }
+  std::memcpy(out, acc.data(), sizeof(float) * size_t(cols));
+  return W4A4_OK;
+}
+
+w4a4_status_t w4a4_smooth_factors(const float* amax_x, const float* amax_w, int K, float alpha,
+                                  float* lambda, float* inv_lambda) {
+  if (!amax_x || !amax_w || !lambda || !inv_lambda || K < 1) return W4A4_ERR_INVALID_ARG;
+  if (!(alpha > 0.0f && alpha < 1.0f)) return W4A4_ERR_INVALID_ARG;
+  std::vector<float> lam(static_cast<size_t>(K)), inv(static_cast<size_t>(K));
+  for (int j = 0; j < K; ++j) {
+    const float ax = amax_x[j], aw = amax_w[j];
+    if (!(ax >= 0.0f) || !(aw >= 0.0f)) return W4A4_ERR_INVALID_ARG;
+    float l = 1.0f;
+    if (ax > 0.0f && aw > 0.0f) {
+      if (alpha == 0.5f)
+        l = float(std::sqrt(double(ax) / double(aw)));
+      else
+        l = float(std::pow(double(ax), double(alpha)) / std::pow(double(aw), 1.0 - double(alpha)));
+    }
+    if (!std::isfinite(l) || !(l >= 0x1p-126f)) return W4A4_ERR_NUMERIC;
+    lam[j] = l;
+    inv[j] = 1.0f / l;
+  }
+  std::memcpy(lambda, lam.data(), sizeof(float) * size_t(K));
+  std::memcpy(inv_lambda, inv.data(), sizeof(float) * size_t(K));
+  return W4A4_OK;
+}
+
+w4a4_status_t w4a4_prepare_weights(const uint16_t* W, int N, int K, const float* lambda, int rank,
+                                   int fmt, const uint16_t* L1_in, const uint16_t* L2_in,
+                                   uint8_t* wq, void* wscale, uint16_t* l1t, uint16_t* l2t,
+                                   uint16_t* L1_out, uint16_t* L2_out) {
+  w4a4_status_t st = check_shape(1, N, K, rank, fmt);
+  if (st != W4A4_OK) return st;
+  if (!W || !lambda || !wq || !wscale) return W4A4_ERR_INVALID_ARG;
+  if ((L1_in == nullptr) != (L2_in == nullptr)) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!l1t || !l2t)) return W4A4_ERR_INVALID_ARG;
+  for (int k = 0; k < K; ++k)
+    if (!std::isfinite(lambda[k]) || !(lambda[k] > 0.0f)) return W4A4_ERR_INVALID_ARG;
+  try {
+    const int np = rows_pad_of(N), rp = rank_pad_of(rank), G = K / W4A4_GROUP;
+    // Ŵ = W · diag(λ) in fp64 (exact: bf16 x fp32 fits in 53 bits)
+    std::vector<double> what(size_t(N) * K);
+    parallel_for(N, [&](int b, int e, int) {
+      for (int n = b; n < e; ++n)
+        for (int k = 0; k < K; ++k)
+          what[size_t(n) * K + k] = double(bf16_to_f32(W[size_t(n) * K + k])) * double(lambda[k]);
+    });
+    // rank-r factors as bf16 values: L1 [K][r], L2 [r][N]
+    std::vector<uint16_t> L1(size_t(K) * rank), L2(size_t(rank) * N);
+    if (rank > 0) {
+      if (L1_in) {
+        std::memcpy(L1.data(), L1_in, L1.size() * 2);
+        std::memcpy(L2.data(), L2_in, L2.size() * 2);
+      } else {
+        std::vector<double> u, sig, v;
+        if (!truncated_svd(what.data(), N, K, rank, u, sig, v)) return W4A4_ERR_NUMERIC;
+        for (int k = 0; k < K; ++k)
+          for (int i = 0; i < rank; ++i)
+            L1[size_t(k) * rank + i] = f32_to_bf16(float(u[size_t(i) * K + k] * sig[i]));
+        for (int i = 0; i < rank; ++i)
+          for (int n = 0; n < N; ++n) L2[size_t(i) * N + n] = f32_to_bf16(float(v[size_t(i) * N + n]));
+      }
+    }
+    std::vector<double> l1d(L1.size()), l2d(L2.size());
+    for (size_t i = 0; i < L1.size(); ++i) l1d[i] = bf16_to_f32(L1[i]);
+    for (size_t i = 0; i < L2.size(); ++i) l2d[i] = bf16_to_f32(L2[i]);
+    // residual and its quantization, one weight row per task
+    const bool mx = fmt == W4A4_FMT_MXFP4_B32;
+    std::memset(wq, 0, size_t(np) * K / 2);
+    std::memset(wscale, 0, mx ? size_t(K / W4A4_MX_BLOCK) * np : size_t(G) * np * 2);
+    parallel_for(N, [&](int b, int e, int) {
+      std::vector<float> rrow(static_cast<size_t>(K));
+      for (int n = b; n < e; ++n) {
+        for (int k = 0; k < K; ++k) {
+          double d = 0.0;
+          for (int i = 0; i < rank; ++i) d += l1d[size_t(k) * rank + i] * l2d[size_t(i) * N + n];
+          rrow[k] = float(what[size_t(n) * K + k] - d);
+        }
+        for (int g = 0; g < G; ++g) {
+          uint8_t* dst = wq + (size_t(g) * np + n) * 32;
+          if (mx) {
+            uint8_t* s8 = static_cast<uint8_t*>(wscale);
+            quant_mxfp4_chunk(rrow.data() + size_t(g) * W4A4_GROUP, dst, &s8[size_t(2 * g) * np + n],
+                              &s8[size_t(2 * g + 1) * np + n]);
+          } else {
+            quant_int4_group(rrow.data() + size_t(g) * W4A4_GROUP, dst,
+                             &static_cast<uint16_t*>(wscale)[size_t(g) * np + n]);
+          }
+        }
+      }
+    });
+    if (rank > 0) {
+      std::memset(l1t, 0, size_t(rp) * K * 2);
+      std::memset(l2t, 0, size_t(np) * rp * 2);
+      for (int k = 0; k < K; ++k)
+        for (int i = 0; i < rank; ++i) l1t[size_t(i) * K + k] = L1[size_t(k) * rank + i];
+      for (int i = 0; i < rank; ++i)
+        for (int n = 0; n < N; ++n) l2t[size_t(n) * rp + i] = L2[size_t(i) * N + n];
+      if (L1_out) std::memcpy(L1_out, L1.data(), L1.size() * 2);
+      if (L2_out) std::memcpy(L2_out, L2.data(), L2.size() * 2);
+    }
+  } catch (const std::bad_alloc&) {
+    return W4A4_ERR_INVALID_ARG;
+  } catch (...) {
+    return W4A4_ERR_NUMERIC;
+  }
+  return W4A4_OK;
+}
+
+w4a4_status_t w4a4_append_lowrank(const uint16_t* l1t, const uint16_t* l2t, int K, int N, int rank,
+                                  const uint16_t* A, const uint16_t* B, int ra,
+                                  uint16_t* l1t_out, uint16_t* l2t_out) {
+  if (!A || !B || !l1t_out || !l2t_out || ra < 1) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!l1t || !l2t)) return W4A4_ERR_INVALID_ARG;
+  const int r2 = rank + ra;
+  w4a4_status_t st = check_shape(1, N, K, r2, W4A4_FMT_INT4_G64);
+  if (st != W4A4_OK) return st;
+  const int np = rows_pad_of(N), rp = rank_pad_of(rank), rp2 = rank_pad_of(r2);
+  std::vector<uint16_t> o1(size_t(rp2) * K, 0), o2(size_t(np) * rp2, 0);
+  for (int i = 0; i < rank; ++i) std::memcpy(&o1[size_t(i) * K], &l1t[size_t(i) * K], size_t(K) * 2);
+  for (int i = 0; i < ra; ++i)
+    for (int k = 0; k < K; ++k) o1[size_t(rank + i) * K + k] = A[size_t(k) * ra + i];
+  for (int n = 0; n < N; ++n) {
+    for (int i = 0; i < rank; ++i) o2[size_t(n) * rp2 + i] = l2t[size_t(n) * rp + i];
+    for (int i = 0; i < ra; ++i) o2[size_t(n) * rp2 + rank + i] = B[size_t(i) * N + n];
+  }
+  std::memcpy(l1t_out, o1.data(), o1.size() * 2);
+  std::memcpy(l2t_out, o2.data(), o2.size() * 2);
+  return W4A4_OK;
+}
+
+w4a4_status_t w4a4_codes_to_canonical(const uint8_t* q, int rows, int K, int fmt, uint8_t* out) {
+  if (!fmt_known(fmt)) return W4A4_ERR_UNSUPPORTED;
+  if (!q || !out || rows < 1 || K < W4A4_GROUP || K % W4A4_GROUP) return W4A4_ERR_INVALID_ARG;
+  const int rp = rows_pad_of(rows), G = K / W4A4_GROUP;
+  for (int r = 0; r < rows; ++r)
+    for (int g = 0; g < G; ++g) {
+      const uint8_t* src = q + (size_t(g) * rp + r) * 32;
+      uint8_t* dst = out + size_t(r) * (K / 2) + size_t(g) * 32;
+      for (int b = 0; b < 32; ++b) {
+        uint8_t byte = src[b];
+        if (fmt == W4A4_FMT_INT4_G64) {
+          auto tc = [](int sm) { int v = (sm & 8) ? -(sm & 7) : (sm & 7); return uint8_t(v & 0xF); };
+          byte = uint8_t(tc(byte & 0xF) | (tc(byte >> 4) << 4));
+        }
+        dst[b] = byte;
+      }
+    }
+  return W4A4_OK;
+}
+
+w4a4_status_t w4a4_scales_to_canonical(const void* s, int rows, int K, int fmt, void* out) {
+  if (!fmt_known(fmt)) return W4A4_ERR_UNSUPPORTED;
+  if (!s || !out || rows < 1 || K < W4A4_GROUP || K % W4A4_GROUP) return W4A4_ERR_INVALID_ARG;
+  const int rp = rows_pad_of(rows);
+  if (fmt == W4A4_FMT_INT4_G64) {
+    const int G = K / W4A4_GROUP;
+    const uint16_t* src = static_cast<const uint16_t*>(s);
+    uint16_t* dst = static_cast<uint16_t*>(out);
+    for (int r = 0; r < rows; ++r)
+      for (int g = 0; g < G; ++g) dst[size_t(r) * G + g] = src[size_t(g) * rp + r];
+  } else {
+    const int B = K / W4A4_MX_BLOCK;
+    const uint8_t* src = static_cast<const uint8_t*>(s);
+    uint8_t* dst = static_cast<uint8_t*>(out);
+    for (int r = 0; r < rows; ++r)
+      for (int b = 0; b < B; ++b) dst[size_t(r) * B + b] = src[size_t(b) * rp + r];
+  }
+  return W4A4_OK;
+}
+
+}  // extern "C"
