@@ -25,7 +25,9 @@ ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32);
 # -ffp-contract=off: every fp32 step that must be bit-reproducible stays a separate IEEE op.
 DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
-                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # MFMA results in VGPRs: the group epilogue reads them with plain VALU FMAs
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-I", INCLUDE, "-I", CSRC]
 HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-pthread", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -32,6 +32,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16f(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
@@ -179,131 +180,226 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
 
 // ===================================================================================
 // Kernel 2: INT4 GEMM + group-scale epilogue + low-rank up projection (+ bias), bf16 out.
-// Block tile BM x BN, 2 x 2 waves, each wave a 2 x 2 grid of 32x32 tiles. One K step = one
-// 64-wide group, double-buffered in LDS. Codes are converted to fp8 once per block while being
-// staged into LDS; scales are staged alongside.
+//
+// Block tile 192 (M) x 256 (N), 8 waves as 2 (M) x 4 (N); each wave owns a 3 x 2 grid of 32x32
+// tiles. One K step = one 64-wide group. Per group:
+//  * the 4-bit codes of A and B and the bf16 scales are copied global -> LDS asynchronously
+//    (global_load_lds) into a ring of I4_NS stages, several groups ahead;
+//  * one block-wide pass converts the codes of the next group to the fp8 carrier (double-
+//    buffered, swizzled 64-byte rows) and the scales to outer-product operands bf16(s * 2^9);
+//  * each wave runs, per tile, one fp8 MFMA (exact integer dot product of the group, times
+//    2^-18), one bf16 MFMA (s_x s_w 2^18) and 16 FMAs into its fp32 accumulators.
+// Staging layouts are sized for 256 rows of A; rows 192..255 carry padding that is never read.
 // ===================================================================================
-constexpr int GB_M = 128, GB_N = 128, G_THREADS = 256;
+constexpr int I4_BM = 192, I4_BN = 256, I4_THREADS = 512;
+constexpr int I4_ROWS = 256;        // staged rows per operand (A uses the first 192)
+constexpr int I4_MT = 3;            // 32-row tiles per wave (M)
+constexpr int I4_GROUP_M = 4;
 
-// LDS chunk swizzle: row r, 16-byte chunk c (0..3) of a 64-byte fp8 row
+// LDS chunk swizzle: row r, 16-byte chunk c (0..3) of a 64-byte fp8 row (conflict-free b128 reads)
 __device__ __forceinline__ int sw_off64(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
 
+// Tile order. Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8),
+// so consecutive logical tiles are handed to the same XCD; logical tiles then sweep N in groups of
+// I4_GROUP_M M-tiles, so the blocks an XCD runs together share A and B slices in its L2.
+__device__ __forceinline__ void tile_of(int b, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int xcd = b & 7, idx = b >> 3, q = nblocks >> 3, rem = nblocks & 7;
+  const int logical = xcd * q + min(xcd, rem) + idx;
+  const int per_group = I4_GROUP_M * tiles_n;
+  const int first_m = (logical / per_group) * I4_GROUP_M;
+  const int gsize = min(tiles_m - first_m, I4_GROUP_M);
+  const int in_group = logical % per_group;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+__device__ __forceinline__ v8i lds_fp8_operand(const uint8_t* base, int row, int lh) {
+  const v4i lo = *reinterpret_cast<const v4i*>(base + sw_off64(row, 2 * lh));
+  const v4i hi = *reinterpret_cast<const v4i*>(base + sw_off64(row, 2 * lh + 1));
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, then s_barrier
+// (global loads in flight are left alone; their consumers wait for them as usual).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+constexpr int I4_KG = 2;                       // groups per pipeline stage (one barrier per stage)
+constexpr int I4_FP8 = I4_ROWS * 64;           // fp8 carriers of one operand, one group
+
 template <int NTR>  // NTR = rank_pad / 16
-__global__ __launch_bounds__(G_THREADS) void gemm_int4_kernel(
+__global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs, const float* __restrict__ xl1,
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
     int m_pad, int n_pad) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][GB_M * 64];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][GB_N * 64];
-  __shared__ uint16_t s_sa[2][GB_M];
-  __shared__ uint16_t s_sb[2][GB_N];
+  // fp8 carriers, [stage buffer][group of the stage][256 rows x 64 B, swizzled]
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][I4_KG][I4_FP8];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][I4_KG][I4_FP8];
+  // outer-product operands bf16(s * 2^9): [buf][group][lane half][A rows 0..255, B rows 256..511];
+  // lane half 1 stays zero
+  __shared__ __attribute__((aligned(16))) uint16_t s_sc[2][I4_KG][2][2 * I4_ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_m = m_pad / GB_M;
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int m0 = tm * GB_M, n0 = tn * GB_N;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int tiles_m = (m_pad + I4_BM - 1) / I4_BM;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, n_pad / I4_BN, tm, tn);
+  const int m0 = tm * I4_BM, n0 = tn * I4_BN;
   const int G = K / W4A4_GROUP;
+  const int S = (G + I4_KG - 1) / I4_KG;
 
-  // global -> register staging: thread loads 16 B of A and 16 B of B (row tid/2, half tid%2)
-  const int lrow = tid >> 1, lhalf = tid & 1;
-  const uint8_t* a_src = xq + ((size_t)(m0 + lrow)) * 32 + lhalf * 16;
-  const uint8_t* b_src = wq + ((size_t)(n0 + lrow)) * 32 + lhalf * 16;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int kg = 0; kg < I4_KG; ++kg) s_sc[b][kg][1][tid] = 0;
+
+  // Staging: per group every thread loads 16 B of A codes (row m0 + tid/2, clamped to the padded
+  // range), 16 B of B codes (row n0 + tid/2) and one scale (tid < 256: A row, else B row).
+  // Groups past the end (odd group count) load the last group and get zero scales.
+  const int arow = min(m0 + (tid >> 1), m_pad - 1);
+  const uint8_t* a_src = xq + (size_t)arow * 32 + 16 * (tid & 1);
+  const uint8_t* b_src = wq + (size_t)(n0 + (tid >> 1)) * 32 + 16 * (tid & 1);
   const size_t a_gstride = (size_t)m_pad * 32, b_gstride = (size_t)n_pad * 32;
+  const uint16_t* s_src = tid < I4_ROWS ? xs + min(m0 + tid, m_pad - 1) : ws + n0 + (tid - I4_ROWS);
+  const size_t s_gstride = tid < I4_ROWS ? (size_t)m_pad : (size_t)n_pad;
+  const int lrow = tid >> 1, lhalf = tid & 1;
 
+  // one group in flight in registers at a time: loaded while the previous group's tiles run,
+  // converted into the next stage buffer right after them
   uint4 ra, rb;
-  uint32_t rs = 0;
+  uint32_t rs;
   auto gload = [&](int g) {
+    g = min(g, G - 1);
     ra = *reinterpret_cast<const uint4*>(a_src + g * a_gstride);
     rb = *reinterpret_cast<const uint4*>(b_src + g * b_gstride);
-    if (tid < 64) rs = *reinterpret_cast<const uint32_t*>(xs + (size_t)g * m_pad + m0 + 2 * tid);
-    else if (tid < 128) rs = *reinterpret_cast<const uint32_t*>(ws + (size_t)g * n_pad + n0 + 2 * (tid - 64));
+    rs = s_src[g * s_gstride];
   };
-  auto lstore = [&](int buf) {
+  auto gstore = [&](int g, int buf, int kg) {
     const uint32_t aw[4] = {ra.x, ra.y, ra.z, ra.w}, bw[4] = {rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint4 fa = make_uint4(fp8_even(aw[2 * j]), fp8_odd(aw[2 * j]), fp8_even(aw[2 * j + 1]), fp8_odd(aw[2 * j + 1]));
-      uint4 fb = make_uint4(fp8_even(bw[2 * j]), fp8_odd(bw[2 * j]), fp8_even(bw[2 * j + 1]), fp8_odd(bw[2 * j + 1]));
-      *reinterpret_cast<uint4*>(&s_a[buf][sw_off64(lrow, 2 * lhalf + j)]) = fa;
-      *reinterpret_cast<uint4*>(&s_b[buf][sw_off64(lrow, 2 * lhalf + j)]) = fb;
+    for (int jj = 0; jj < 2; ++jj) {
+      *reinterpret_cast<uint4*>(&s_a[buf][kg][sw_off64(lrow, 2 * lhalf + jj)]) =
+          make_uint4(fp8_even(aw[2 * jj]), fp8_odd(aw[2 * jj]), fp8_even(aw[2 * jj + 1]), fp8_odd(aw[2 * jj + 1]));
+      *reinterpret_cast<uint4*>(&s_b[buf][kg][sw_off64(lrow, 2 * lhalf + jj)]) =
+          make_uint4(fp8_even(bw[2 * jj]), fp8_odd(bw[2 * jj]), fp8_even(bw[2 * jj + 1]), fp8_odd(bw[2 * jj + 1]));
     }
-    if (tid < 64) *reinterpret_cast<uint32_t*>(&s_sa[buf][2 * tid]) = rs;
-    else if (tid < 128) *reinterpret_cast<uint32_t*>(&s_sb[buf][2 * (tid - 64)]) = rs;
+    const float sv = g < G ? bf16f(rs) * 512.f : 0.f;  // groups past the end contribute nothing
+    s_sc[buf][kg][0][tid] = (uint16_t)bf16_rne(sv);
   };
 
-  v16f acc[2][2];
+  v16f acc[I4_MT][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < I4_MT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
   const v16f zero16 = {};
   const int lr = lane & 31, lh = lane >> 5;
+  const int arow0 = wm * (32 * I4_MT) + lr, bcol0 = wn * 64 + lr;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    if (g + 1 < G) gload(g + 1);
-    v8i A[2], B[2];
-    v4i OA[2], OB[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = wm * 64 + i * 32 + lr;
-      const v4i lo = *reinterpret_cast<const v4i*>(&s_a[buf][sw_off64(row, 2 * lh)]);
-      const v4i hi = *reinterpret_cast<const v4i*>(&s_a[buf][sw_off64(row, 2 * lh + 1)]);
-      A[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      // exact outer-product operand: bf16(s_x * 2^9) at k = 0 (lanes 0..31), zero elsewhere
-      const uint32_t sx = lh == 0 ? bf16_rne(bf16f(s_sa[buf][wm * 64 + i * 32 + lr]) * 512.f) : 0u;
-      OA[i] = v4i{(int)sx, 0, 0, 0};
-    }
+  for (int kg = 0; kg < I4_KG; ++kg) {
+    gload(kg);
+    gstore(kg, 0, kg);
+  }
+  lds_barrier();
+  for (int st = 0; st < S; ++st) {
+    const int buf = st & 1;
+    const int gnext = (st + 1) * I4_KG;  // first group of the next stage
+    gload(gnext);
+    // ---- the stage's I4_KG groups, 6 tiles each, software-pipelined across the group boundary:
+    // the carrier MFMA of tile t+1 is issued before the 16 FMAs of tile t, its outer product
+    // right after them (two carrier products and one scale product live at a time).
+    constexpr int T = 2 * I4_MT;
+    v8i Bv[2], Bn[2];
+    v4s OB[2], OBn[2];
+    v8i Av, An;
+    v4s OA, OAn;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = wn * 64 + j * 32 + lr;
-      const v4i lo = *reinterpret_cast<const v4i*>(&s_b[buf][sw_off64(col, 2 * lh)]);
-      const v4i hi = *reinterpret_cast<const v4i*>(&s_b[buf][sw_off64(col, 2 * lh + 1)]);
-      B[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const uint32_t sw = lh == 0 ? bf16_rne(bf16f(s_sb[buf][wn * 64 + j * 32 + lr]) * 512.f) : 0u;
-      OB[j] = v4i{(int)sw, 0, 0, 0};
+      Bv[j] = lds_fp8_operand(s_b[buf][0], bcol0 + j * 32, lh);
+      OB[j] = v4s{(short)s_sc[buf][0][lh][I4_ROWS + bcol0 + j * 32], 0, 0, 0};
     }
+    Av = lds_fp8_operand(s_a[buf][0], arow0, lh);
+    OA = v4s{(short)s_sc[buf][0][lh][arow0], 0, 0, 0};
+    An = lds_fp8_operand(s_a[buf][0], arow0 + 32, lh);
+    OAn = v4s{(short)s_sc[buf][0][lh][arow0 + 32], 0, 0, 0};
+    v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[0], zero16, 0, 0, 0, 127, 0, 127);
+    v16f sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(OA, OB[0], zero16, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int u = 0; u < I4_KG * T; ++u) {
+      const int kg = u / T, t = u % T, i = t >> 1, j = t & 1;
+      const int u1 = u + 1, kg1 = u1 / T, t1 = u1 % T, i1 = t1 >> 1, j1 = t1 & 1;
+      v16f pn;
+      if (u1 < I4_KG * T) {
+        if (t1 == 0) {  // next group of the stage: switch to the prefetched operands
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[i], B[j], zero16, 0, 0, 0, 127, 0, 127);
-        const v16f s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(OA[i]), as_bf16x8(OB[j]), zero16, 0, 0, 0);
+          for (int jj = 0; jj < 2; ++jj) {
+            Bv[jj] = Bn[jj];
+            OB[jj] = OBn[jj];
+          }
+        }
+        if (j1 == 0) {
+          Av = An;
+          OA = OAn;
+        }
+        // prefetch: the next row tile's A operand, and (during the last row tile) the next group's B
+        // operands and its first A operand
+        const int pr_u = u1 + 1;  // tile whose A is prefetched when the row changes
+        if (j1 == 0 && pr_u < I4_KG * T) {
+          const int pkg = (u1 + 2) / T, pt = (u1 + 2) % T;
+          if (pt < T && pkg < I4_KG) {
+            An = lds_fp8_operand(s_a[buf][pkg], arow0 + (pt >> 1) * 32, lh);
+            OAn = v4s{(short)s_sc[buf][pkg][lh][arow0 + (pt >> 1) * 32], 0, 0, 0};
+          }
+        }
+        if (t1 == T - 2 && kg1 + 1 < I4_KG) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], s[v], acc[i][j][v]);
+          for (int jj = 0; jj < 2; ++jj) {
+            Bn[jj] = lds_fp8_operand(s_b[buf][kg1 + 1], bcol0 + jj * 32, lh);
+            OBn[jj] = v4s{(short)s_sc[buf][kg1 + 1][lh][I4_ROWS + bcol0 + jj * 32], 0, 0, 0};
+          }
+        }
+        pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[j1], zero16, 0, 0, 0, 127, 0, 127);
       }
-    if (g + 1 < G) lstore(buf ^ 1);
-    __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc[v], acc[i][j][v]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (u1 < I4_KG * T) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(OA, OB[j1], zero16, 0, 0, 0);
+        p = pn;
+      }
+      if (t == T - 1) {  // a group of this stage is done: stage one group of the next stage
+        gstore(gnext + kg, buf ^ 1, kg);  // at the last stage this writes an unused buffer
+        if (kg + 1 < I4_KG) gload(gnext + kg + 1);
+      }
+    }
+    lds_barrier();
   }
 
-  // low-rank up projection: acc += bf16(t) · L2 over k = rank index (32x32x16 bf16 MFMA)
+  // low-rank up projection: acc += bf16(t) · L2 over k = rank index (32x32x16 bf16 MFMA);
+  // rows past the padded range (last M tile) read a valid row and are never stored
   if (NTR > 0) {
     constexpr int RP = NTR * 16;
 #pragma unroll
     for (int kk = 0; kk < RP; kk += 16) {
-      v4i TA[2];
+      v4i LB[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const float* tp = xl1 + (size_t)(m0 + wm * 64 + i * 32 + lr) * RP + kk + 8 * lh;
+      for (int j = 0; j < 2; ++j)
+        LB[j] = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 64 + j * 32 + lr) * RP + kk + 8 * lh);
+#pragma unroll
+      for (int i = 0; i < I4_MT; ++i) {
+        const int trow = min(m0 + wm * (32 * I4_MT) + i * 32 + lr, m_pad - 1);
+        const float* tp = xl1 + (size_t)trow * RP + kk + 8 * lh;
         const float4 t0 = *reinterpret_cast<const float4*>(tp);
         const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
-        TA[i] = v4i{(int)(bf16_rne(t0.x) | (bf16_rne(t0.y) << 16)), (int)(bf16_rne(t0.z) | (bf16_rne(t0.w) << 16)),
-                    (int)(bf16_rne(t1.x) | (bf16_rne(t1.y) << 16)), (int)(bf16_rne(t1.z) | (bf16_rne(t1.w) << 16))};
-      }
+        const v4i TA = v4i{(int)(bf16_rne(t0.x) | (bf16_rne(t0.y) << 16)), (int)(bf16_rne(t0.z) | (bf16_rne(t0.w) << 16)),
+                           (int)(bf16_rne(t1.x) | (bf16_rne(t1.y) << 16)), (int)(bf16_rne(t1.z) | (bf16_rne(t1.w) << 16))};
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const v4i lb = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 64 + j * 32 + lr) * RP + kk + 8 * lh);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(TA[i]), as_bf16x8(lb), acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(TA), as_bf16x8(LB[j]), acc[i][j], 0, 0, 0);
       }
     }
   }
@@ -315,14 +411,19 @@ __global__ __launch_bounds__(G_THREADS) void gemm_int4_kernel(
     if (col >= N) continue;
     const float bcol = bias ? bf16f(bias[col]) : 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < I4_MT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+        const int row = m0 + wm * (32 * I4_MT) + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
         if (row < M) Y[(size_t)row * ldy + col] = (uint16_t)bf16_rne(acc[i][j][v] + bcol);
       }
   }
 }
+
+// ===================================================================================
+// MXFP4 tiling (kernel 3): block 128 x 128, 2 x 2 waves of 64 x 64.
+// ===================================================================================
+constexpr int GB_M = 128, GB_N = 128, G_THREADS = 256;
 
 // ===================================================================================
 // Kernel 3: MXFP4 GEMM (E2M1 x E2M1 with E8M0 block scales applied by the MFMA) + low-rank
@@ -478,12 +579,11 @@ template <int NTR>
 hipError_t launch_gemm(int fmt, const uint8_t* xq, const void* xs, const float* xl1, const uint8_t* wq,
                        const void* ws, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy, int M,
                        int N, int K, int m_pad, int n_pad, hipStream_t st) {
-  const dim3 grid((m_pad / GB_M) * (n_pad / GB_N));
   if (fmt == W4A4_FMT_INT4_G64)
-    hipLaunchKernelGGL((gemm_int4_kernel<NTR>), grid, dim3(G_THREADS), 0, st, xq, static_cast<const uint16_t*>(xs),
+    hipLaunchKernelGGL((gemm_int4_kernel<NTR>), dim3(((m_pad + I4_BM - 1) / I4_BM) * (n_pad / I4_BN)), dim3(I4_THREADS), 0, st, xq, static_cast<const uint16_t*>(xs),
                        xl1, wq, static_cast<const uint16_t*>(ws), l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
   else
-    hipLaunchKernelGGL((gemm_mxfp4_kernel<NTR>), grid, dim3(G_THREADS), 0, st, xq, static_cast<const uint8_t*>(xs),
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<NTR>), dim3((m_pad / GB_M) * (n_pad / GB_N)), dim3(G_THREADS), 0, st, xq, static_cast<const uint8_t*>(xs),
                        xl1, wq, static_cast<const uint8_t*>(ws), l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
   return hipGetLastError();
 }
