@@ -75,9 +75,15 @@ const char* w4a4_status_str(w4a4_status_t status);
  * Buffer sizes and layouts. K must be a positive multiple of 64 for both formats (the MXFP4
  * kernels step K by two 32-blocks). m_pad = roundup(M, 256), n_pad = roundup(N, 256),
  * rank_pad = roundup(rank, 16) (0 for rank 0). Layouts (G64 = K/64, B32 = K/32):
- *   wq     [G64][n_pad][32] bytes : the 64 codes of (row, group); code k of the group at byte
- *                                   k/2, low nibble for even k. INT4 nibbles are sign-magnitude
- *                                   (bit 3 sign, bits 0-2 |q|); MXFP4 nibbles are E2M1 codes.
+ *   wq     [G64][n_pad][32] bytes : the 64 codes of (row, group), 4 bits each.
+ *            MXFP4: code k of the group at byte k/2, low nibble for even k (E2M1 codes).
+ *            INT4 (folded FP6 image): the 8 little-endian dwords d0..d7 hold codes 16j..16j+15
+ *            in the pair (d[2j], d[2j+1]). With F_f = (q < 0) << 5 | |q| for code 16j + f (the
+ *            FP6 E2M3 encoding of q/8) and the 96-bit image I = Σ_f F_f << 6f split into dwords
+ *            o0, o1, o2: d[2j] = (o0 & 0xE79E79E7) | (o1 & 0x18618618),
+ *            d[2j+1] = (o1 & 0x61861861) | (o2 & 0x9E79E79E). (Bits 3-4 of every 6-bit field
+ *            are zero, which leaves room for o1 in o0 and o2.) The GEMM unfolds this into FP6
+ *            MFMA operands with four AND / AND-OR operations per 16 codes.
  *   wscale INT4: [G64][n_pad] bf16;  MXFP4: [B32][n_pad] E8M0 bytes (e + 127)
  *   l1t    [rank_pad][K] bf16   : L1ᵀ, rows >= rank are zero
  *   l2t    [n_pad][rank_pad] bf16 : L2ᵀ, columns >= rank are zero

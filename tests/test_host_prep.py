@@ -116,16 +116,37 @@ def test_weight_codes_bit_exact_given_oracle_factors(shape, fmt):
     assert not wq[:, n:].any()
 
 
+def _unfold_int4(raw):
+    """Decode the folded INT4 layout of include/w4a4.h: per row, 8 dwords; the pair (d[2j], d[2j+1])
+    holds the FP6 E2M3 image (fields sign<<5 | |q| at bit 6f) of codes 16j..16j+15."""
+    d = raw.reshape(raw.shape[0], 8, 4).astype(np.uint64)
+    d = d[..., 0] | (d[..., 1] << 8) | (d[..., 2] << 16) | (d[..., 3] << 24)
+    out = np.zeros((raw.shape[0], 64), np.int16)
+    for j in range(4):
+        lo, hi = d[:, 2 * j], d[:, 2 * j + 1]
+        img = [lo & 0xE79E79E7, (lo & 0x18618618) | (hi & 0x61861861), hi & 0x9E79E79E]
+        bits = [int(x) for x in img[0]], [int(x) for x in img[1]], [int(x) for x in img[2]]
+        for f in range(16):
+            fld = np.array([((o0 | (o1 << 32) | (o2 << 64)) >> (6 * f)) & 63
+                            for o0, o1, o2 in zip(*bits)], np.int16)
+            assert not (fld & 0b011000).any(), "exponent bits of an FP6 carrier must be zero"
+            out[:, 16 * j + f] = np.where(fld & 32, -(fld & 7), fld & 7)
+    return out
+
+
 def test_padding_and_layout_of_weight_codes():
-    """Library layout: [G][n_pad][32], sign-magnitude nibbles for INT4."""
+    """Library layout: [G][n_pad][32]; INT4 codes folded FP6 images, MXFP4 plain E2M1 nibbles."""
     d = synth.make_layer(8, 64, 3, n_outliers=1, outlier_scale=10.0, seed=3)
     lam = np.ones(64, np.float32)
     prep = w4.prepare_weights(d["w"], lam, 0, "int4_g64")
     q, s = O.quant_int4_g64(O.bf16_bits_to_f32(d["w"]))
     raw = prep["wq"].reshape(1, 256, 32)[0, :3]
-    lo, hi = (raw & 0xF).astype(np.int16), (raw >> 4).astype(np.int16)
-    sm = lambda v: np.where(v & 8, -(v & 7), v & 7)
-    assert np.array_equal(sm(lo), q[:, 0::2]) and np.array_equal(sm(hi), q[:, 1::2])
+    assert np.array_equal(_unfold_int4(raw), q)
+    assert (np.abs(q) >= 6).any() and (q < 0).any()      # the case exercises signs and large codes
+    prep = w4.prepare_weights(d["w"], lam, 0, "mxfp4_b32")
+    qm, _ = O.quant_mxfp4_b32(O.bf16_bits_to_f32(d["w"]))
+    raw = prep["wq"].reshape(1, 256, 32)[0, :3]
+    assert np.array_equal(raw & 0xF, qm[:, 0::2]) and np.array_equal(raw >> 4, qm[:, 1::2])
 
 
 def _lowrank_err(w_hat, l1_bits, l2_bits):

@@ -7,12 +7,15 @@
 // quantization with 16-bit scales; FP4 E2M1 with qmax 6).
 //
 // MFMA use on gfx950:
-//  * INT4 x INT4 products run on the fp8 (E4M3) MFMA v_mfma_scale_f32_32x32x64_f8f6f4. A 4-bit
-//    code q (|q| <= 7) is carried as the E4M3 subnormal sign|0000|mag, whose value is q * 2^-9,
-//    so every product and every partial sum of one 64-wide group is exact in fp32 (the result
-//    is 2^-18 * Σ q_x q_w, |Σ| <= 3136). One 32x32x64 MFMA is exactly one group.
+//  * INT4 x INT4 products run on the scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4 with FP6
+//    (E2M3) operands, which issues at twice the fp8 rate. A code q (|q| <= 7) is carried as the
+//    E2M3 subnormal sign|00|mag, whose value is q / 8, so every product and every partial sum of
+//    one 64-wide group is exact in fp32 (the result is Σ q_x q_w / 64, |Σ| <= 3136). One
+//    32x32x64 MFMA is exactly one group. The codes stay 4 bits wide in memory: each 16-code run
+//    is stored as its 96-bit FP6 image folded into 64 bits (the zero exponent bits of the outer
+//    dwords hold the middle dword), and four AND/AND-OR ops per 16 codes unfold it for the MFMA.
 //  * The per-group scale product s_x[m,g] * s_w[n,g] of a 32x32 tile is produced as an exact
-//    outer product by one bf16 MFMA (v_mfma_f32_32x32x16_bf16 with one non-zero k), so the
+//    outer product by one bf16 MFMA (v_mfma_f32_32x32x8_bf16 with one non-zero k), so the
 //    group epilogue costs one fp32 FMA per output element.
 //  * FP4 (E2M1) codes with E8M0 block scales run on the same scaled MFMA with the block scales
 //    applied by the hardware.
@@ -44,11 +47,22 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 __device__ __forceinline__ v8bf as_bf16x8(v4i v) { return __builtin_bit_cast(v8bf, v); }
 
-// Sign-magnitude INT4 nibbles (8 per dword) -> fp8 E4M3 subnormal carriers (4 per dword).
-// Even codes (low nibble of each byte) and odd codes (high nibble) go to separate dwords; A and B
-// operands use the same split, so each MFMA dot product still pairs equal k.
-__device__ __forceinline__ uint32_t fp8_even(uint32_t w) { return (w & 0x07070707u) | ((w << 4) & 0x80808080u); }
-__device__ __forceinline__ uint32_t fp8_odd(uint32_t w) { return ((w >> 4) & 0x07070707u) | (w & 0x80808080u); }
+// Folded FP6 layout of INT4 codes. A run of 16 codes c_0..c_15 has the FP6 image
+// I = Σ_f (sign_f << 5 | |c_f|) << 6f (96 bits, dwords o0 o1 o2). Bits 3 and 4 of every 6-bit field
+// (the exponent) are zero, which frees exactly the bit positions of the middle dword: stored are
+// lo = (o0 & C0) | (o1 & C34) and hi = (o1 & C05) | (o2 & C2), with masks over p = bit % 6:
+// C0 = {0,1,2,5}, C34 = {3,4}, C05 = {0,5}, C2 = {1,2,3,4}.
+constexpr uint32_t FOLD_C0 = 0xE79E79E7u, FOLD_C34 = 0x18618618u, FOLD_C05 = 0x61861861u, FOLD_C2 = 0x9E79E79Eu;
+
+__device__ __forceinline__ uint2 fold_fp6(uint32_t o0, uint32_t o1, uint32_t o2) {
+  return make_uint2((o0 & FOLD_C0) | (o1 & FOLD_C34), (o1 & FOLD_C05) | (o2 & FOLD_C2));
+}
+
+// 16 B of folded codes (32 codes of one row, one half of a group) -> the 6-dword FP6 operand
+__device__ __forceinline__ v8i unfold_fp6(v4i d) {
+  return v8i{d[0] & (int)FOLD_C0, (d[0] & (int)FOLD_C34) | (d[1] & (int)FOLD_C05), d[1] & (int)FOLD_C2,
+             d[2] & (int)FOLD_C0, (d[2] & (int)FOLD_C34) | (d[3] & (int)FOLD_C05), d[3] & (int)FOLD_C2, 0, 0};
+}
 
 // ===================================================================================
 // Kernel 1: activation side. One block = 16 rows x all of K; QA_WAVES waves split the groups.
@@ -64,6 +78,7 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
     float* __restrict__ xl1) {
   extern __shared__ float s_part[];  // [QA_WAVES][QA_ROWS][NT*16]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // lane (r, kc) owns row r and the 16 consecutive values 16 kc .. 16 kc + 15 of each group
   const int r = lane & 15, kc = lane >> 4;
   const int m = blockIdx.x * QA_ROWS + r;
   const bool valid = m < M;
@@ -74,13 +89,13 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
 
   const uint16_t* xrow = X + (size_t)(valid ? m : 0) * ldx;
   for (int g = wave; g < G; g += QA_WAVES) {
-    const int k0 = g * W4A4_GROUP + kc * 8;
+    const int k0 = g * W4A4_GROUP + kc * 16;
     float xh[2][8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint4 xv = valid ? *reinterpret_cast<const uint4*>(xrow + k0 + 32 * h) : make_uint4(0, 0, 0, 0);
-      const float4 i0 = *reinterpret_cast<const float4*>(inv_lambda + k0 + 32 * h);
-      const float4 i1 = *reinterpret_cast<const float4*>(inv_lambda + k0 + 32 * h + 4);
+      uint4 xv = valid ? *reinterpret_cast<const uint4*>(xrow + k0 + 8 * h) : make_uint4(0, 0, 0, 0);
+      const float4 i0 = *reinterpret_cast<const float4*>(inv_lambda + k0 + 8 * h);
+      const float4 i1 = *reinterpret_cast<const float4*>(inv_lambda + k0 + 8 * h + 4);
       const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
       const float il[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
@@ -89,7 +104,7 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
         xh[h][e] = bf16f(bits) * il[e];  // one fp32 multiply (no contraction: nothing to fuse)
       }
     }
-    uint8_t* qdst = xq + ((size_t)g * m_pad + blockIdx.x * QA_ROWS + r) * 32 + kc * 4;
+    uint2* qdst = reinterpret_cast<uint2*>(xq + ((size_t)g * m_pad + blockIdx.x * QA_ROWS + r) * 32 + kc * 8);
     if (FMT == W4A4_FMT_INT4_G64) {
       float amax = 0.f;
 #pragma unroll
@@ -101,38 +116,41 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
       float s = bf16f(bf16_rne(amax / 7.0f));
       if (!(s >= 0x1p-126f)) s = 0.f;
       const float inv = s != 0.f ? 1.0f / s : 0.f;
+      uint32_t img[3] = {0u, 0u, 0u};  // FP6 image of the lane's 16 codes
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t word = 0;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float y = __builtin_rintf(xh[h][e] * inv);
           y = fminf(7.f, fmaxf(-7.f, y));
           const int q = (int)y;
-          const uint32_t nib = (q < 0 ? 8u : 0u) | (uint32_t)(q < 0 ? -q : q);
-          word |= nib << (4 * e);
+          const uint32_t fld = (q < 0 ? 32u : 0u) | (uint32_t)(q < 0 ? -q : q);
+          const int bit = 6 * (8 * h + e);  // compile-time after unrolling
+          img[bit >> 5] |= fld << (bit & 31);
+          if ((bit & 31) > 26) img[(bit >> 5) + 1] |= fld >> (32 - (bit & 31));
         }
-        *reinterpret_cast<uint32_t*>(qdst + 16 * h) = word;
-      }
+      *qdst = fold_fp6(img[0], img[1], img[2]);
       if (kc == 0) static_cast<uint16_t*>(xscale)[(size_t)g * m_pad + blockIdx.x * QA_ROWS + r] = (uint16_t)bf16_rne(s);
     } else {
+      // the lane's 16 values lie in 32-block kc / 2, shared with lane kc ^ 1
+      float amax = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float amax = 0.f;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xh[h][e]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      int e8;
+      if (amax == 0.f) {
+        e8 = -127;
+      } else {
         int ex;
-        int e8;
-        if (amax == 0.f) {
-          e8 = -127;
-        } else {
-          const float mant = frexpf(amax, &ex);  // amax = mant * 2^ex, mant in [0.5, 1)
-          e8 = mant <= 0.75f ? ex - 3 : ex - 2;
-          e8 = max(-127, min(127, e8));
-        }
-        uint32_t word = 0;
+        const float mant = frexpf(amax, &ex);  // amax = mant * 2^ex, mant in [0.5, 1)
+        e8 = mant <= 0.75f ? ex - 3 : ex - 2;
+        e8 = max(-127, min(127, e8));
+      }
+      uint32_t word[2] = {0u, 0u};
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float y = ldexpf(xh[h][e], -e8);
@@ -140,12 +158,11 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
           const uint32_t idx = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
                              : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
           const uint32_t nib = ((__float_as_uint(y) >> 28) & 8u) | idx;
-          word |= nib << (4 * e);
+          word[h] |= nib << (4 * e);
         }
-        *reinterpret_cast<uint32_t*>(qdst + 16 * h) = word;
-        if (kc == 0)
-          static_cast<uint8_t*>(xscale)[(size_t)(2 * g + h) * m_pad + blockIdx.x * QA_ROWS + r] = (uint8_t)(e8 + 127);
-      }
+      *qdst = make_uint2(word[0], word[1]);
+      if ((kc & 1) == 0)
+        static_cast<uint8_t*>(xscale)[(size_t)(2 * g + (kc >> 1)) * m_pad + blockIdx.x * QA_ROWS + r] = (uint8_t)(e8 + 127);
     }
     if (NT > 0) {
 #pragma unroll
@@ -155,7 +172,7 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
         for (int d = 0; d < 4; ++d) a[d] = (int)(bf16_rne(xh[h][2 * d]) | (bf16_rne(xh[h][2 * d + 1]) << 16));
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-          const v4i b = *reinterpret_cast<const v4i*>(l1t + (size_t)(c * 16 + r) * K + k0 + 32 * h);
+          const v4i b = *reinterpret_cast<const v4i*>(l1t + (size_t)(c * 16 + r) * K + k0 + 8 * h);
           acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc[c], 0, 0, 0);
         }
       }
@@ -181,23 +198,26 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
 // ===================================================================================
 // Kernel 2: INT4 GEMM + group-scale epilogue + low-rank up projection (+ bias), bf16 out.
 //
-// Block tile 192 (M) x 256 (N), 8 waves as 2 (M) x 4 (N); each wave owns a 3 x 2 grid of 32x32
-// tiles. One K step = one 64-wide group. Per group:
-//  * the 4-bit codes of A and B and the bf16 scales are copied global -> LDS asynchronously
-//    (global_load_lds) into a ring of I4_NS stages, several groups ahead;
-//  * one block-wide pass converts the codes of the next group to the fp8 carrier (double-
-//    buffered, swizzled 64-byte rows) and the scales to outer-product operands bf16(s * 2^9);
-//  * each wave runs, per tile, one fp8 MFMA (exact integer dot product of the group, times
-//    2^-18), one bf16 MFMA (s_x s_w 2^18) and 16 FMAs into its fp32 accumulators.
-// Staging layouts are sized for 256 rows of A; rows 192..255 carry padding that is never read.
+// Block tile I4_BM (M) x 256 (N), 8 waves as 2 (M) x 4 (N); each wave owns an I4_MT x 2 grid of
+// 32x32 tiles. One K step = one 64-wide group; I4_KG groups form a pipeline stage with one
+// barrier. Per group:
+//  * every thread copies 16 B of folded A codes, 16 B of folded B codes and one scale
+//    global -> registers -> LDS, one group ahead of the tiles that use them (double-buffered
+//    stages; rows are 32 B, halves swizzled for conflict-free 16-byte reads); the scales go to
+//    LDS as outer-product operands bf16(s * 2^3);
+//  * each wave unfolds its A and B operands to FP6 and runs, per tile, one FP6 MFMA (exact
+//    integer dot product of the group, times 2^-6), one bf16 MFMA (s_x s_w 2^6) and 16 FMAs into
+//    its fp32 accumulators.
+// Staging layouts are sized for 256 rows of A; rows past I4_BM carry padding that is never read.
 // ===================================================================================
 constexpr int I4_BM = 192, I4_BN = 256, I4_THREADS = 512;
 constexpr int I4_ROWS = 256;        // staged rows per operand (A uses the first 192)
 constexpr int I4_MT = 3;            // 32-row tiles per wave (M)
 constexpr int I4_GROUP_M = 4;
 
-// LDS chunk swizzle: row r, 16-byte chunk c (0..3) of a 64-byte fp8 row (conflict-free b128 reads)
-__device__ __forceinline__ int sw_off64(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+// LDS swizzle of 32-byte code rows: row r, 16-byte half h (rows 8..15 of every 16 swap halves, so
+// the 16-byte reads of 8 consecutive lanes cover all 64 banks)
+__device__ __forceinline__ int sw_off32(int r, int h) { return r * 32 + 16 * (h ^ ((r >> 3) & 1)); }
 
 // Tile order. Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8),
 // so consecutive logical tiles are handed to the same XCD; logical tiles then sweep N in groups of
@@ -213,10 +233,8 @@ __device__ __forceinline__ void tile_of(int b, int nblocks, int tiles_m, int til
   tn = in_group / gsize;
 }
 
-__device__ __forceinline__ v8i lds_fp8_operand(const uint8_t* base, int row, int lh) {
-  const v4i lo = *reinterpret_cast<const v4i*>(base + sw_off64(row, 2 * lh));
-  const v4i hi = *reinterpret_cast<const v4i*>(base + sw_off64(row, 2 * lh + 1));
-  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+__device__ __forceinline__ v8i lds_fp6_operand(const uint8_t* base, int row, int lh) {
+  return unfold_fp6(*reinterpret_cast<const v4i*>(base + sw_off32(row, lh)));
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, then s_barrier
@@ -224,7 +242,7 @@ __device__ __forceinline__ v8i lds_fp8_operand(const uint8_t* base, int row, int
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 constexpr int I4_KG = 2;                       // groups per pipeline stage (one barrier per stage)
-constexpr int I4_FP8 = I4_ROWS * 64;           // fp8 carriers of one operand, one group
+constexpr int I4_STG = I4_ROWS * 32;           // folded codes of one operand, one group
 
 template <int NTR>  // NTR = rank_pad / 16
 __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
@@ -232,10 +250,10 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
     int m_pad, int n_pad) {
-  // fp8 carriers, [stage buffer][group of the stage][256 rows x 64 B, swizzled]
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][I4_KG][I4_FP8];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][I4_KG][I4_FP8];
-  // outer-product operands bf16(s * 2^9): [buf][group][lane half][A rows 0..255, B rows 256..511];
+  // folded codes, [stage buffer][group of the stage][256 rows x 32 B, swizzled]
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][I4_KG][I4_STG];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][I4_KG][I4_STG];
+  // outer-product operands bf16(s * 2^3): [buf][group][lane half][A rows 0..255, B rows 256..511];
   // lane half 1 stays zero
   __shared__ __attribute__((aligned(16))) uint16_t s_sc[2][I4_KG][2][2 * I4_ROWS];
 
@@ -275,15 +293,9 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
     rs = s_src[g * s_gstride];
   };
   auto gstore = [&](int g, int buf, int kg) {
-    const uint32_t aw[4] = {ra.x, ra.y, ra.z, ra.w}, bw[4] = {rb.x, rb.y, rb.z, rb.w};
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      *reinterpret_cast<uint4*>(&s_a[buf][kg][sw_off64(lrow, 2 * lhalf + jj)]) =
-          make_uint4(fp8_even(aw[2 * jj]), fp8_odd(aw[2 * jj]), fp8_even(aw[2 * jj + 1]), fp8_odd(aw[2 * jj + 1]));
-      *reinterpret_cast<uint4*>(&s_b[buf][kg][sw_off64(lrow, 2 * lhalf + jj)]) =
-          make_uint4(fp8_even(bw[2 * jj]), fp8_odd(bw[2 * jj]), fp8_even(bw[2 * jj + 1]), fp8_odd(bw[2 * jj + 1]));
-    }
-    const float sv = g < G ? bf16f(rs) * 512.f : 0.f;  // groups past the end contribute nothing
+    *reinterpret_cast<uint4*>(&s_a[buf][kg][sw_off32(lrow, lhalf)]) = ra;
+    *reinterpret_cast<uint4*>(&s_b[buf][kg][sw_off32(lrow, lhalf)]) = rb;
+    const float sv = g < G ? bf16f(rs) * 8.f : 0.f;  // groups past the end contribute nothing
     s_sc[buf][kg][0][tid] = (uint16_t)bf16_rne(sv);
   };
 
@@ -318,14 +330,14 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
     v4s OA, OAn;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      Bv[j] = lds_fp8_operand(s_b[buf][0], bcol0 + j * 32, lh);
+      Bv[j] = lds_fp6_operand(s_b[buf][0], bcol0 + j * 32, lh);
       OB[j] = v4s{(short)s_sc[buf][0][lh][I4_ROWS + bcol0 + j * 32], 0, 0, 0};
     }
-    Av = lds_fp8_operand(s_a[buf][0], arow0, lh);
+    Av = lds_fp6_operand(s_a[buf][0], arow0, lh);
     OA = v4s{(short)s_sc[buf][0][lh][arow0], 0, 0, 0};
-    An = lds_fp8_operand(s_a[buf][0], arow0 + 32, lh);
+    An = lds_fp6_operand(s_a[buf][0], arow0 + 32, lh);
     OAn = v4s{(short)s_sc[buf][0][lh][arow0 + 32], 0, 0, 0};
-    v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[0], zero16, 0, 0, 0, 127, 0, 127);
+    v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[0], zero16, 2, 2, 0, 127, 0, 127);
     v16f sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(OA, OB[0], zero16, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < I4_KG * T; ++u) {
@@ -350,18 +362,18 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
         if (j1 == 0 && pr_u < I4_KG * T) {
           const int pkg = (u1 + 2) / T, pt = (u1 + 2) % T;
           if (pt < T && pkg < I4_KG) {
-            An = lds_fp8_operand(s_a[buf][pkg], arow0 + (pt >> 1) * 32, lh);
+            An = lds_fp6_operand(s_a[buf][pkg], arow0 + (pt >> 1) * 32, lh);
             OAn = v4s{(short)s_sc[buf][pkg][lh][arow0 + (pt >> 1) * 32], 0, 0, 0};
           }
         }
         if (t1 == T - 2 && kg1 + 1 < I4_KG) {
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
-            Bn[jj] = lds_fp8_operand(s_b[buf][kg1 + 1], bcol0 + jj * 32, lh);
+            Bn[jj] = lds_fp6_operand(s_b[buf][kg1 + 1], bcol0 + jj * 32, lh);
             OBn[jj] = v4s{(short)s_sc[buf][kg1 + 1][lh][I4_ROWS + bcol0 + jj * 32], 0, 0, 0};
           }
         }
-        pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[j1], zero16, 0, 0, 0, 127, 0, 127);
+        pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[j1], zero16, 2, 2, 0, 127, 0, 127);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -429,8 +441,6 @@ constexpr int GB_M = 128, GB_N = 128, G_THREADS = 256;
 // Kernel 3: MXFP4 GEMM (E2M1 x E2M1 with E8M0 block scales applied by the MFMA) + low-rank
 // epilogue. Same tiling as kernel 2; one K step = 64 = two 32-blocks (lanes 0-31 / 32-63).
 // ===================================================================================
-__device__ __forceinline__ int sw_off32(int r, int h) { return r * 32 + 16 * (h ^ ((r >> 3) & 1)); }
-
 template <int NTR>
 __global__ __launch_bounds__(G_THREADS) void gemm_mxfp4_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ xl1,

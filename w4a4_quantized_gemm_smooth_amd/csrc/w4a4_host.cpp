@@ -62,6 +62,56 @@ void parallel_for(int n, const std::function<void(int, int, int)>& fn) {
   for (auto& t : ts) t.join();
 }
 
+// ------------------------------------------------------------------------------ code layouts
+// INT4 codes are stored folded (the layout the GEMM unfolds into FP6 MFMA operands): per row and
+// group 32 bytes = 8 little-endian dwords; dwords 2j and 2j+1 hold codes 16j .. 16j+15 of the
+// group. With F_f = (sign << 5) | |q| (the E2M3 subnormal carrying q / 8) for code 16j + f, the
+// 96-bit image I = Σ_f F_f << 6f has dwords o0 o1 o2, and the pair is
+// lo = (o0 & C0) | (o1 & C34), hi = (o1 & C05) | (o2 & C2) (masks over bit % 6: C0 = {0,1,2,5},
+// C34 = {3,4}, C05 = {0,5}, C2 = {1,2,3,4}).
+constexpr uint32_t kFoldC0 = 0xE79E79E7u, kFoldC34 = 0x18618618u, kFoldC05 = 0x61861861u, kFoldC2 = 0x9E79E79Eu;
+
+// nib: 64 sign-magnitude codes (bit 3 = sign) -> 32 folded bytes
+void fold_int4_group(const uint8_t* nib, uint8_t* out32) {
+  for (int j = 0; j < 4; ++j) {
+    uint32_t img[3] = {0, 0, 0};
+    for (int f = 0; f < 16; ++f) {
+      const uint8_t c = nib[16 * j + f];
+      const uint64_t fld = uint64_t(((c & 8u) << 2) | (c & 7u));
+      const int bit = 6 * f;
+      const uint64_t w = fld << (bit & 31);
+      img[bit >> 5] |= uint32_t(w);
+      if ((bit >> 5) + 1 < 3) img[(bit >> 5) + 1] |= uint32_t(w >> 32);
+    }
+    const uint32_t lo = (img[0] & kFoldC0) | (img[1] & kFoldC34);
+    const uint32_t hi = (img[1] & kFoldC05) | (img[2] & kFoldC2);
+    for (int b = 0; b < 4; ++b) {
+      out32[8 * j + b] = uint8_t(lo >> (8 * b));
+      out32[8 * j + 4 + b] = uint8_t(hi >> (8 * b));
+    }
+  }
+}
+
+// 32 folded bytes -> 64 codes as signed values
+void unfold_int4_group(const uint8_t* in32, int* q) {
+  for (int j = 0; j < 4; ++j) {
+    uint32_t lo = 0, hi = 0;
+    for (int b = 0; b < 4; ++b) {
+      lo |= uint32_t(in32[8 * j + b]) << (8 * b);
+      hi |= uint32_t(in32[8 * j + 4 + b]) << (8 * b);
+    }
+    const uint32_t img[3] = {lo & kFoldC0, (lo & kFoldC34) | (hi & kFoldC05), hi & kFoldC2};
+    for (int f = 0; f < 16; ++f) {
+      const int bit = 6 * f;
+      uint64_t w = img[bit >> 5];
+      if ((bit >> 5) + 1 < 3) w |= uint64_t(img[(bit >> 5) + 1]) << 32;
+      const uint32_t fld = uint32_t(w >> (bit & 31)) & 63u;
+      const int mag = int(fld & 7u);
+      q[16 * j + f] = (fld & 32u) ? -mag : mag;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------ quantizers
 // One INT4 group (64 values): s = bf16(max|v| / 7); q = clamp(rint(v * (1/s))); a scale below
 // 2^-126 is stored as 0 with zero codes. Symmetric scaling bounds |v * (1/s)| by
@@ -82,7 +132,7 @@ void quant_int4_group(const float* v, uint8_t* out32, uint16_t* scale_bits) {
       nib[k] = uint8_t((q < 0 ? 8 : 0) | (q < 0 ? -q : q));
     }
   }
-  for (int i = 0; i < W4A4_GROUP / 2; ++i) out32[i] = uint8_t(nib[2 * i] | (nib[2 * i + 1] << 4));
+  fold_int4_group(nib, out32);
 }
 
 // e = the smallest integer with 6 * 2^e >= amax, in [-127, 127]; -127 for amax == 0.
@@ -476,13 +526,12 @@ w4a4_status_t w4a4_codes_to_canonical(const uint8_t* q, int rows, int K, int fmt
     for (int g = 0; g < G; ++g) {
       const uint8_t* src = q + (size_t(g) * rp + r) * 32;
       uint8_t* dst = out + size_t(r) * (K / 2) + size_t(g) * 32;
-      for (int b = 0; b < 32; ++b) {
-        uint8_t byte = src[b];
-        if (fmt == W4A4_FMT_INT4_G64) {
-          auto tc = [](int sm) { int v = (sm & 8) ? -(sm & 7) : (sm & 7); return uint8_t(v & 0xF); };
-          byte = uint8_t(tc(byte & 0xF) | (tc(byte >> 4) << 4));
-        }
-        dst[b] = byte;
+      if (fmt == W4A4_FMT_INT4_G64) {
+        int v[W4A4_GROUP];
+        unfold_int4_group(src, v);
+        for (int b = 0; b < 32; ++b) dst[b] = uint8_t((v[2 * b] & 0xF) | ((v[2 * b + 1] & 0xF) << 4));
+      } else {
+        std::memcpy(dst, src, 32);
       }
     }
   return W4A4_OK;
