@@ -198,22 +198,18 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
 // ===================================================================================
 // Kernel 2: INT4 GEMM + group-scale epilogue + low-rank up projection (+ bias), bf16 out.
 //
-// Block tile I4_BM (M) x 256 (N), 8 waves as 2 (M) x 4 (N); each wave owns an I4_MT x 2 grid of
-// 32x32 tiles. One K step = one 64-wide group; I4_KG groups form a pipeline stage with one
-// barrier. Per group:
-//  * every thread copies 16 B of folded A codes, 16 B of folded B codes and one scale
-//    global -> registers -> LDS, one group ahead of the tiles that use them (double-buffered
-//    stages; rows are 32 B, halves swizzled for conflict-free 16-byte reads); the scales go to
-//    LDS as outer-product operands bf16(s * 2^3);
-//  * each wave unfolds its A and B operands to FP6 and runs, per tile, one FP6 MFMA (exact
-//    integer dot product of the group, times 2^-6), one bf16 MFMA (s_x s_w 2^6) and 16 FMAs into
-//    its fp32 accumulators.
-// Staging layouts are sized for 256 rows of A; rows past I4_BM carry padding that is never read.
+// Block tile 256 (M) x 256 (N), 8 waves as 2 (M) x 4 (N); each wave owns a 4 x 2 grid of 32x32
+// tiles. One K step = one 64-wide group. The folded codes and the bf16 scales of each group are
+// copied global -> LDS by the LDS DMA path (global_load_lds) into a ring of I4_NS slots, so up to
+// I4_NS - 2 groups are in flight while one is computed; one barrier per group publishes the next
+// slot. Per group each wave unfolds its A and B operands to FP6 and runs, per tile, one FP6 MFMA
+// with E8M0 scales 2^3 x 2^3 (the exact integer dot product of the group), one bf16 MFMA (the
+// exact outer product s_x s_w of the raw bf16 scales) and 16 FMAs into its fp32 accumulators.
 // ===================================================================================
-constexpr int I4_BM = 192, I4_BN = 256, I4_THREADS = 512;
-constexpr int I4_ROWS = 256;        // staged rows per operand (A uses the first 192)
-constexpr int I4_MT = 3;            // 32-row tiles per wave (M)
+constexpr int I4_BM = 256, I4_BN = 256, I4_THREADS = 512;
+constexpr int I4_MT = 4;            // 32-row tiles per wave (M)
 constexpr int I4_GROUP_M = 4;
+constexpr int I4_NS = 6;            // ring slots (groups)
 
 // LDS swizzle of 32-byte code rows: row r, 16-byte half h (rows 8..15 of every 16 swap halves, so
 // the 16-byte reads of 8 consecutive lanes cover all 64 banks)
@@ -233,16 +229,21 @@ __device__ __forceinline__ void tile_of(int b, int nblocks, int tiles_m, int til
   tn = in_group / gsize;
 }
 
-__device__ __forceinline__ v8i lds_fp6_operand(const uint8_t* base, int row, int lh) {
-  return unfold_fp6(*reinterpret_cast<const v4i*>(base + sw_off32(row, lh)));
+// One ring slot: the folded codes of 256 A rows and 256 B rows (32 B each, swizzled) and their
+// bf16 scales (A rows 0..255, then B rows). Each slot is its own LDS object, so the compiler can
+// tell the DMA writes into one slot from the reads of another.
+struct I4Slot {
+  uint8_t a[256 * 32];
+  uint8_t b[256 * 32];
+  uint16_t s[512];
+};
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left alone), visible to the compiler's wait tracking
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
-
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, then s_barrier
-// (global loads in flight are left alone; their consumers wait for them as usual).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-constexpr int I4_KG = 2;                       // groups per pipeline stage (one barrier per stage)
-constexpr int I4_STG = I4_ROWS * 32;           // folded codes of one operand, one group
 
 template <int NTR>  // NTR = rank_pad / 16
 __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
@@ -250,53 +251,34 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
     int m_pad, int n_pad) {
-  // folded codes, [stage buffer][group of the stage][256 rows x 32 B, swizzled]
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][I4_KG][I4_STG];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][I4_KG][I4_STG];
-  // outer-product operands bf16(s * 2^3): [buf][group][lane half][A rows 0..255, B rows 256..511];
-  // lane half 1 stays zero
-  __shared__ __attribute__((aligned(16))) uint16_t s_sc[2][I4_KG][2][2 * I4_ROWS];
+  __shared__ __attribute__((aligned(16))) I4Slot sl0, sl1, sl2, sl3, sl4, sl5;
+  I4Slot* const ring[I4_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5};
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
-  const int tiles_m = (m_pad + I4_BM - 1) / I4_BM;
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, n_pad / I4_BN, tm, tn);
+  tile_of(blockIdx.x, gridDim.x, m_pad / I4_BM, n_pad / I4_BN, tm, tn);
   const int m0 = tm * I4_BM, n0 = tn * I4_BN;
   const int G = K / W4A4_GROUP;
-  const int S = (G + I4_KG - 1) / I4_KG;
 
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int kg = 0; kg < I4_KG; ++kg) s_sc[b][kg][1][tid] = 0;
-
-  // Staging: per group every thread loads 16 B of A codes (row m0 + tid/2, clamped to the padded
-  // range), 16 B of B codes (row n0 + tid/2) and one scale (tid < 256: A row, else B row).
-  // Groups past the end (odd group count) load the last group and get zero scales.
-  const int arow = min(m0 + (tid >> 1), m_pad - 1);
-  const uint8_t* a_src = xq + (size_t)arow * 32 + 16 * (tid & 1);
-  const uint8_t* b_src = wq + (size_t)(n0 + (tid >> 1)) * 32 + 16 * (tid & 1);
+  // ---- DMA sources. Instruction w of an operand fills LDS bytes [1024 w, 1024 w + 1024) of the
+  // slot, lane i the 16 bytes at 1024 w + 16 i = row 32 w + i / 2, stored half i & 1; the lane
+  // loads the global half that the swizzle puts there. Scales: wave w copies 128 scales (256 B)
+  // of block w & 3 (A rows, then B rows); waves w and w + 4 write the same bytes.
+  const int drow = 32 * wave + (lane >> 1);
+  const int dhalf = (lane & 1) ^ ((drow >> 3) & 1);
+  const uint8_t* a_src = xq + (size_t)(m0 + drow) * 32 + 16 * dhalf;
+  const uint8_t* b_src = wq + (size_t)(n0 + drow) * 32 + 16 * dhalf;
   const size_t a_gstride = (size_t)m_pad * 32, b_gstride = (size_t)n_pad * 32;
-  const uint16_t* s_src = tid < I4_ROWS ? xs + min(m0 + tid, m_pad - 1) : ws + n0 + (tid - I4_ROWS);
-  const size_t s_gstride = tid < I4_ROWS ? (size_t)m_pad : (size_t)n_pad;
-  const int lrow = tid >> 1, lhalf = tid & 1;
-
-  // one group in flight in registers at a time: loaded while the previous group's tiles run,
-  // converted into the next stage buffer right after them
-  uint4 ra, rb;
-  uint32_t rs;
-  auto gload = [&](int g) {
+  const int sblk = wave & 3;
+  const uint16_t* s_src = sblk < 2 ? xs + m0 + 128 * sblk + 2 * lane : ws + n0 + 128 * (sblk - 2) + 2 * lane;
+  const size_t s_gstride = sblk < 2 ? (size_t)m_pad : (size_t)n_pad;
+  // 3 vector-memory instructions per wave and group; groups past the end reload the last group
+  auto dma = [&](int g, I4Slot* sl) {
     g = min(g, G - 1);
-    ra = *reinterpret_cast<const uint4*>(a_src + g * a_gstride);
-    rb = *reinterpret_cast<const uint4*>(b_src + g * b_gstride);
-    rs = s_src[g * s_gstride];
-  };
-  auto gstore = [&](int g, int buf, int kg) {
-    *reinterpret_cast<uint4*>(&s_a[buf][kg][sw_off32(lrow, lhalf)]) = ra;
-    *reinterpret_cast<uint4*>(&s_b[buf][kg][sw_off32(lrow, lhalf)]) = rb;
-    const float sv = g < G ? bf16f(rs) * 8.f : 0.f;  // groups past the end contribute nothing
-    s_sc[buf][kg][0][tid] = (uint16_t)bf16_rne(sv);
+    __builtin_amdgcn_global_load_lds(a_src + g * a_gstride, sl->a + 1024 * wave, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b_src + g * b_gstride, sl->b + 1024 * wave, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(s_src + g * s_gstride, sl->s + 128 * sblk, 4, 0, 0);
   };
 
   v16f acc[I4_MT][2];
@@ -308,91 +290,100 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   const v16f zero16 = {};
   const int lr = lane & 31, lh = lane >> 5;
-  const int arow0 = wm * (32 * I4_MT) + lr, bcol0 = wn * 64 + lr;
+  const int arow0 = wm * 128 + lr, bcol0 = wn * 64 + lr;
+  // operand byte offsets inside a slot (tile i / j adds 1024 i / 1024 j)
+  const int a_off = sw_off32(arow0, lh), b_off = sw_off32(bcol0, lh);
 
+  // operands of the scale outer product: bf16 scale at k = 0 (lanes 0..31), zero elsewhere;
+  // groups past the end get zero scales. Kept as one register, widened at the MFMA.
+  auto sc_val = [&](const I4Slot* sl, int row, bool live) -> uint32_t {
+    const uint32_t s = sl->s[row];
+    return (lh == 0 && live) ? s : 0u;
+  };
+  auto sc_op = [](uint32_t s) { return v4s{(short)s, 0, 0, 0}; };
+  auto a_raw = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i); };
+  auto b_raw = [&](const I4Slot* sl, int j) { return *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j); };
+
+  // prologue: groups 0 .. NS-2 in flight; group 0 visible; its first operands in registers
 #pragma unroll
-  for (int kg = 0; kg < I4_KG; ++kg) {
-    gload(kg);
-    gstore(kg, 0, kg);
+  for (int s = 0; s < I4_NS - 1; ++s) dma(s, ring[s]);
+  wait_vmcnt<3 * (I4_NS - 2)>();
+  __builtin_amdgcn_s_barrier();
+  v8i Bv[2], Av;
+  uint32_t OB[2], OA;
+  v4i An_raw, Bn_raw[2];
+  uint32_t OAn, OBn[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    Bv[j] = unfold_fp6(b_raw(ring[0], j));
+    OB[j] = sc_val(ring[0], 256 + bcol0 + 32 * j, true);
   }
-  lds_barrier();
-  for (int st = 0; st < S; ++st) {
-    const int buf = st & 1;
-    const int gnext = (st + 1) * I4_KG;  // first group of the next stage
-    gload(gnext);
-    // ---- the stage's I4_KG groups, 6 tiles each, software-pipelined across the group boundary:
-    // the carrier MFMA of tile t+1 is issued before the 16 FMAs of tile t, its outer product
-    // right after them (two carrier products and one scale product live at a time).
-    constexpr int T = 2 * I4_MT;
-    v8i Bv[2], Bn[2];
-    v4s OB[2], OBn[2];
-    v8i Av, An;
-    v4s OA, OAn;
+  Av = unfold_fp6(a_raw(ring[0], 0));
+  OA = sc_val(ring[0], arow0, true);
+  An_raw = a_raw(ring[0], 1);
+  OAn = sc_val(ring[0], arow0 + 32, true);
+
+  constexpr int T = 2 * I4_MT;
+  v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[0], zero16, 2, 2, 0, 130, 0, 130);
+  v16f sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sc_op(OA), sc_op(OB[0]), zero16, 0, 0, 0);
+
+  for (int g0 = 0; g0 < G; g0 += I4_NS) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      Bv[j] = lds_fp6_operand(s_b[buf][0], bcol0 + j * 32, lh);
-      OB[j] = v4s{(short)s_sc[buf][0][lh][I4_ROWS + bcol0 + j * 32], 0, 0, 0};
-    }
-    Av = lds_fp6_operand(s_a[buf][0], arow0, lh);
-    OA = v4s{(short)s_sc[buf][0][lh][arow0], 0, 0, 0};
-    An = lds_fp6_operand(s_a[buf][0], arow0 + 32, lh);
-    OAn = v4s{(short)s_sc[buf][0][lh][arow0 + 32], 0, 0, 0};
-    v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[0], zero16, 2, 2, 0, 127, 0, 127);
-    v16f sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(OA, OB[0], zero16, 0, 0, 0);
+    for (int u = 0; u < I4_NS; ++u) {
+      const int g = g0 + u;
+      const I4Slot* cur = ring[u];
+      const I4Slot* nxt = ring[(u + 1) % I4_NS];
+      // group g + 1 has landed in every wave's share of its slot; everyone is done with slot g - 1
+      wait_vmcnt<3 * (I4_NS - 3)>();
+      __builtin_amdgcn_s_barrier();
+      dma(g + I4_NS - 1, ring[(u + I4_NS - 1) % I4_NS]);
+      const bool live0 = g < G, live1 = g + 1 < G;
+      // ---- the group's 8 tiles, software-pipelined: the FP6 MFMA of tile t+1 is issued before the
+      // 16 FMAs of tile t and its outer product right after them; the last tile's successor is
+      // tile 0 of group g + 1, whose operands are read from the next slot during this group
 #pragma unroll
-    for (int u = 0; u < I4_KG * T; ++u) {
-      const int kg = u / T, t = u % T, i = t >> 1, j = t & 1;
-      const int u1 = u + 1, kg1 = u1 / T, t1 = u1 % T, i1 = t1 >> 1, j1 = t1 & 1;
-      v16f pn;
-      if (u1 < I4_KG * T) {
-        if (t1 == 0) {  // next group of the stage: switch to the prefetched operands
+      for (int t = 0; t < T; ++t) {
+        const int i = t >> 1, j = t & 1;
+        const int t1 = t + 1, i1 = (t1 % T) >> 1, j1 = t1 & 1;
+        if (t1 == T - 2) {  // next group's B operands and scales
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
-            Bv[jj] = Bn[jj];
+            Bn_raw[jj] = b_raw(nxt, jj);
+            OBn[jj] = sc_val(nxt, 256 + bcol0 + 32 * jj, live1);
+          }
+        }
+        if (t1 == T) {  // switch to group g + 1
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            Bv[jj] = unfold_fp6(Bn_raw[jj]);
             OB[jj] = OBn[jj];
           }
         }
-        if (j1 == 0) {
-          Av = An;
+        if (j1 == 0) {  // new tile row: take the prefetched A operand, prefetch the following one
+          Av = unfold_fp6(An_raw);
           OA = OAn;
-        }
-        // prefetch: the next row tile's A operand, and (during the last row tile) the next group's B
-        // operands and its first A operand
-        const int pr_u = u1 + 1;  // tile whose A is prefetched when the row changes
-        if (j1 == 0 && pr_u < I4_KG * T) {
-          const int pkg = (u1 + 2) / T, pt = (u1 + 2) % T;
-          if (pt < T && pkg < I4_KG) {
-            An = lds_fp6_operand(s_a[buf][pkg], arow0 + (pt >> 1) * 32, lh);
-            OAn = v4s{(short)s_sc[buf][pkg][lh][arow0 + (pt >> 1) * 32], 0, 0, 0};
+          if (t1 < T - 2) {
+            An_raw = a_raw(cur, i1 + 1);
+            OAn = sc_val(cur, arow0 + 32 * (i1 + 1), live0);
+          } else {  // rows 0 and 1 of the next group follow rows 3 and 0
+            const int r1 = t1 == T - 2 ? 0 : 1;
+            An_raw = a_raw(nxt, r1);
+            OAn = sc_val(nxt, arow0 + 32 * r1, live1);
           }
         }
-        if (t1 == T - 2 && kg1 + 1 < I4_KG) {
+        const v16f pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[j1], zero16, 2, 2, 0, 130, 0, 130);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            Bn[jj] = lds_fp6_operand(s_b[buf][kg1 + 1], bcol0 + jj * 32, lh);
-            OBn[jj] = v4s{(short)s_sc[buf][kg1 + 1][lh][I4_ROWS + bcol0 + jj * 32], 0, 0, 0};
-          }
-        }
-        pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[j1], zero16, 2, 2, 0, 127, 0, 127);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc[v], acc[i][j][v]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (u1 < I4_KG * T) {
-        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(OA, OB[j1], zero16, 0, 0, 0);
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc[v], acc[i][j][v]);
+        __builtin_amdgcn_sched_barrier(0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sc_op(OA), sc_op(OB[j1]), zero16, 0, 0, 0);
         p = pn;
       }
-      if (t == T - 1) {  // a group of this stage is done: stage one group of the next stage
-        gstore(gnext + kg, buf ^ 1, kg);  // at the last stage this writes an unused buffer
-        if (kg + 1 < I4_KG) gload(gnext + kg + 1);
-      }
     }
-    lds_barrier();
   }
+  wait_vmcnt<0>();  // no LDS DMA may outlive the block
 
-  // low-rank up projection: acc += bf16(t) · L2 over k = rank index (32x32x16 bf16 MFMA);
-  // rows past the padded range (last M tile) read a valid row and are never stored
+  // low-rank up projection: acc += bf16(t) · L2 over k = rank index (32x32x16 bf16 MFMA)
   if (NTR > 0) {
     constexpr int RP = NTR * 16;
 #pragma unroll
@@ -403,7 +394,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
         LB[j] = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 64 + j * 32 + lr) * RP + kk + 8 * lh);
 #pragma unroll
       for (int i = 0; i < I4_MT; ++i) {
-        const int trow = min(m0 + wm * (32 * I4_MT) + i * 32 + lr, m_pad - 1);
+        const int trow = m0 + wm * 128 + i * 32 + lr;
         const float* tp = xl1 + (size_t)trow * RP + kk + 8 * lh;
         const float4 t0 = *reinterpret_cast<const float4*>(tp);
         const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
@@ -426,7 +417,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
     for (int i = 0; i < I4_MT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * (32 * I4_MT) + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+        const int row = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
         if (row < M) Y[(size_t)row * ldy + col] = (uint16_t)bf16_rne(acc[i][j][v] + bcol);
       }
   }
@@ -590,7 +581,7 @@ hipError_t launch_gemm(int fmt, const uint8_t* xq, const void* xs, const float* 
                        const void* ws, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy, int M,
                        int N, int K, int m_pad, int n_pad, hipStream_t st) {
   if (fmt == W4A4_FMT_INT4_G64)
-    hipLaunchKernelGGL((gemm_int4_kernel<NTR>), dim3(((m_pad + I4_BM - 1) / I4_BM) * (n_pad / I4_BN)), dim3(I4_THREADS), 0, st, xq, static_cast<const uint16_t*>(xs),
+    hipLaunchKernelGGL((gemm_int4_kernel<NTR>), dim3((m_pad / I4_BM) * (n_pad / I4_BN)), dim3(I4_THREADS), 0, st, xq, static_cast<const uint16_t*>(xs),
                        xl1, wq, static_cast<const uint16_t*>(ws), l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
   else
     hipLaunchKernelGGL((gemm_mxfp4_kernel<NTR>), dim3((m_pad / GB_M) * (n_pad / GB_N)), dim3(G_THREADS), 0, st, xq, static_cast<const uint8_t*>(xs),
