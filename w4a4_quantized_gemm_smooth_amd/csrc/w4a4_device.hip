@@ -200,8 +200,8 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
 //
 // Block tile 256 (M) x 256 (N), 8 waves as 2 (M) x 4 (N); each wave owns a 4 x 2 grid of 32x32
 // tiles. One K step = one 64-wide group. The folded codes and the bf16 scales of each group are
-// copied global -> LDS by the LDS DMA path (global_load_lds) into a ring of I4_NS slots, so up to
-// I4_NS - 2 groups are in flight while one is computed; one barrier per group publishes the next
+// copied global -> LDS by the LDS DMA path (global_load_lds) into a ring of I4_NS slots, issued
+// four groups before their first reader; one barrier per two groups publishes the next slots
 // slot. Per group each wave unfolds its A and B operands to FP6 and runs, per tile, one FP6 MFMA
 // with E8M0 scales 2^3 x 2^3 (the exact integer dot product of the group), one bf16 MFMA (the
 // exact outer product s_x s_w of the raw bf16 scales) and 16 FMAs into its fp32 accumulators.
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
 constexpr int I4_BM = 256, I4_BN = 256, I4_THREADS = 512;
 constexpr int I4_MT = 4;            // 32-row tiles per wave (M)
 constexpr int I4_GROUP_M = 4;
-constexpr int I4_NS = 6;            // ring slots (groups)
+constexpr int I4_NS = 8;            // ring slots (groups); even
 
 // LDS swizzle of 32-byte code rows: row r, 16-byte half h (rows 8..15 of every 16 swap halves, so
 // the 16-byte reads of 8 consecutive lanes cover all 64 banks)
@@ -251,10 +251,11 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
     int m_pad, int n_pad) {
-  __shared__ __attribute__((aligned(16))) I4Slot sl0, sl1, sl2, sl3, sl4, sl5;
-  I4Slot* const ring[I4_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5};
+  __shared__ __attribute__((aligned(16))) I4Slot sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7;
+  I4Slot* const ring[I4_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5, &sl6, &sl7};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps derived addresses scalar
   const int wm = wave >> 2, wn = wave & 3;
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, m_pad / I4_BM, n_pad / I4_BN, tm, tn);
@@ -267,18 +268,20 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
   // of block w & 3 (A rows, then B rows); waves w and w + 4 write the same bytes.
   const int drow = 32 * wave + (lane >> 1);
   const int dhalf = (lane & 1) ^ ((drow >> 3) & 1);
-  const uint8_t* a_src = xq + (size_t)(m0 + drow) * 32 + 16 * dhalf;
-  const uint8_t* b_src = wq + (size_t)(n0 + drow) * 32 + 16 * dhalf;
-  const size_t a_gstride = (size_t)m_pad * 32, b_gstride = (size_t)n_pad * 32;
+  const uint32_t c_lane = drow * 32 + 16 * dhalf;   // byte offset of the lane's 16 B in a code tile
   const int sblk = wave & 3;
-  const uint16_t* s_src = sblk < 2 ? xs + m0 + 128 * sblk + 2 * lane : ws + n0 + 128 * (sblk - 2) + 2 * lane;
-  const size_t s_gstride = sblk < 2 ? (size_t)m_pad : (size_t)n_pad;
-  // 3 vector-memory instructions per wave and group; groups past the end reload the last group
+  const uint32_t s_lane = 4 * lane;                  // byte offset of the lane's two scales
+  // 3 vector-memory instructions per wave and group (uniform base + 32-bit lane offset); groups
+  // past the end reload the last group
   auto dma = [&](int g, I4Slot* sl) {
     g = min(g, G - 1);
-    __builtin_amdgcn_global_load_lds(a_src + g * a_gstride, sl->a + 1024 * wave, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(b_src + g * b_gstride, sl->b + 1024 * wave, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(s_src + g * s_gstride, sl->s + 128 * sblk, 4, 0, 0);
+    const uint8_t* a_base = xq + ((size_t)g * m_pad + m0) * 32;
+    const uint8_t* b_base = wq + ((size_t)g * n_pad + n0) * 32;
+    const uint8_t* s_base = sblk < 2 ? reinterpret_cast<const uint8_t*>(xs + (size_t)g * m_pad + m0 + 128 * sblk)
+                                     : reinterpret_cast<const uint8_t*>(ws + (size_t)g * n_pad + n0 + 128 * (sblk - 2));
+    __builtin_amdgcn_global_load_lds(a_base + c_lane, sl->a + 1024 * wave, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b_base + c_lane, sl->b + 1024 * wave, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(s_base + s_lane, sl->s + 128 * sblk, 4, 0, 0);
   };
 
   v16f acc[I4_MT][2];
@@ -304,10 +307,10 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
   auto a_raw = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i); };
   auto b_raw = [&](const I4Slot* sl, int j) { return *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j); };
 
-  // prologue: groups 0 .. NS-2 in flight; group 0 visible; its first operands in registers
+  // prologue: groups 0 .. NS-3 in flight; group 0 visible; its first operands in registers
 #pragma unroll
-  for (int s = 0; s < I4_NS - 1; ++s) dma(s, ring[s]);
-  wait_vmcnt<3 * (I4_NS - 2)>();
+  for (int s = 0; s < I4_NS - 2; ++s) dma(s, ring[s]);
+  wait_vmcnt<3 * (I4_NS - 3)>();
   __builtin_amdgcn_s_barrier();
   v8i Bv[2], Av;
   uint32_t OB[2], OA;
@@ -333,10 +336,14 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
       const int g = g0 + u;
       const I4Slot* cur = ring[u];
       const I4Slot* nxt = ring[(u + 1) % I4_NS];
-      // group g + 1 has landed in every wave's share of its slot; everyone is done with slot g - 1
-      wait_vmcnt<3 * (I4_NS - 3)>();
-      __builtin_amdgcn_s_barrier();
-      dma(g + I4_NS - 1, ring[(u + I4_NS - 1) % I4_NS]);
+      if (u % 2 == 0) {
+        // groups g+1 and g+2 have landed in every wave's share of their slots; everyone is done
+        // with slots g-2 and g-1, which take groups g+NS-2 and g+NS-1
+        wait_vmcnt<3 * (I4_NS - 5)>();
+        __builtin_amdgcn_s_barrier();
+        dma(g + I4_NS - 2, ring[(u + I4_NS - 2) % I4_NS]);
+        dma(g + I4_NS - 1, ring[(u + I4_NS - 1) % I4_NS]);
+      }
       const bool live0 = g < G, live1 = g + 1 < G;
       // ---- the group's 8 tiles, software-pipelined: the FP6 MFMA of tile t+1 is issued before the
       // 16 FMAs of tile t and its outer product right after them; the last tile's successor is
