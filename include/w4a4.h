@@ -88,7 +88,9 @@ const char* w4a4_status_str(w4a4_status_t status);
  *   l1t    [rank_pad][K] bf16   : L1ᵀ, rows >= rank are zero
  *   l2t    [n_pad][rank_pad] bf16 : L2ᵀ, columns >= rank are zero
  *   xq, xscale : as wq, wscale with m_pad rows
- *   xl1    [m_pad][rank_pad] fp32 : t = bf16(X̂)·L1 (fp32 accumulation)
+ *   xl1    fp32, first [m_pad][rank_pad] : t = bf16(X̂)·L1 (fp32 accumulation); the rest of the
+ *          buffer (when the size returned here exceeds m_pad·rank_pad·4 bytes) is scratch that
+ *          w4a4_quantize_act uses for per-K-slice partial sums of t. 0 bytes when rank == 0.
  * Returns W4A4_ERR_INVALID_ARG for M, N < 1, K not a positive multiple of 64, rank outside
  * [0, min(N, K, W4A4_MAX_RANK)], or out == NULL; W4A4_ERR_UNSUPPORTED for an unknown fmt.
  */

@@ -59,7 +59,7 @@ def gpu_layer(d, lam, inv, rank, fmt, ref_prep, bias=None, x_rows=None, pad_cols
                y=O.bf16_bits_to_f32(y.view(torch.int16).cpu().numpy().view(np.uint16)))
     if rank:
         rp = prep["rank_pad"]
-        out["t"] = a["xl1"].cpu().numpy().reshape(-1, rp)[:M]
+        out["t"] = a["xl1"].cpu().numpy()[: (M + 255) // 256 * 256 * rp].reshape(-1, rp)[:M]  # t, then scratch
     return out
 
 
@@ -215,7 +215,7 @@ def test_full_size_lora_merge():
     y = layer(x)
     torch.cuda.synchronize()
     M = d["M"]
-    t = layer.act_buffers(M)["xl1"].cpu().numpy().reshape(-1, 48)[:M]
+    t = layer.act_buffers(M)["xl1"].cpu().numpy()[: (M + 255) // 256 * 256 * 48].reshape(-1, 48)[:M]
     yg = O.bf16_bits_to_f32(y.view(torch.int16).cpu().numpy().view(np.uint16))
     rows = _sample_rows(M, seed=3)
     check_y(dict(y=yg), oracle_rows(d, inv, merged, "int4_g64", rows), rows)

@@ -36,6 +36,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef int v6i __attribute__((ext_vector_type(6)));
 
 __device__ __forceinline__ float bf16f(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
@@ -65,46 +66,109 @@ __device__ __forceinline__ v8i unfold_fp6(v4i d) {
 }
 
 // ===================================================================================
-// Kernel 1: activation side. One block = 16 rows x all of K; QA_WAVES waves split the groups.
-// Per row and group: X̂ = fp32(x * inv_lambda); codes + scales; t += bf16(X̂) · L1 (MFMA).
+// Kernel 1: activation side. Per row and group: X̂ = fp32(x * inv_lambda); codes + scales;
+// t += bf16(X̂) · L1 (MFMA). One block = 128 rows (8 waves of 16) x one slice of at most
+// QA_MAX_GS groups: every wave issues the X loads of all its groups at once, and the slice's
+// 1/λ and L1 rows are copied into LDS by the LDS DMA path, shared by the 8 row tiles. With
+// several slices the partial t of a slice goes to its own scratch plane; t_reduce_kernel sums
+// the planes in slice order.
 // ===================================================================================
-constexpr int QA_WAVES = 8;
-constexpr int QA_ROWS = 16;
+constexpr int QA_WAVES = QA_BLOCK_ROWS / 16;
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left alone), visible to the compiler's wait tracking
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {  // v_cvt_pk_bf16_f32, nearest-even
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), bf2));
+}
+
+// LDS bytes of one block: 1/λ (16 B slots), L1 rows of RP rank columns padded by one slot, in
+// whole 64-slot DMA instructions
+constexpr int qa_lds_slots(int rp, int gs) { return (gs * 16 + rp * (gs * 8 + 1) + 63) / 64 * 64; }
 
 template <int FMT, int NT>  // NT = rank_pad / 16 (0 when there is no low-rank branch)
-__global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
-    const uint16_t* __restrict__ X, int M, int K, int ldx, const float* __restrict__ inv_lambda,
-    const uint16_t* __restrict__ l1t, int m_pad, uint8_t* __restrict__ xq, void* __restrict__ xscale,
+__global__ __launch_bounds__(QA_WAVES * 64, NT <= 2 ? 4 : 2) void quantize_act_kernel(
+    // X is not restrict: its loads must stay ahead of the counted wait below
+    const uint16_t* X, int M, int K, int ldx, const float* __restrict__ inv_lambda,
+    const uint16_t* __restrict__ l1t, int m_pad, int gs, uint8_t* __restrict__ xq, void* __restrict__ xscale,
     float* __restrict__ xl1) {
-  extern __shared__ float s_part[];  // [QA_WAVES][QA_ROWS][NT*16]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // lane (r, kc) owns row r and the 16 consecutive values 16 kc .. 16 kc + 15 of each group
-  const int r = lane & 15, kc = lane >> 4;
-  const int m = blockIdx.x * QA_ROWS + r;
-  const bool valid = m < M;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int RP = NT * 16;
   const int G = K / W4A4_GROUP;
-  v4f acc[NT > 0 ? NT : 1];
-#pragma unroll
-  for (int c = 0; c < (NT > 0 ? NT : 1); ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int nsl = (G + gs - 1) / gs;
+  const int rb = blockIdx.x / nsl, sl = blockIdx.x % nsl;
+  const int g0 = sl * gs, ng = min(gs, G - g0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // lane (r, kc) owns row r of the wave's tile and the 16 consecutive values 16 kc .. 16 kc + 15
+  // of each group
+  const int r = lane & 15, kc = lane >> 4;
+  const int row = rb * QA_BLOCK_ROWS + wave * 16 + r;
+  const bool valid = row < M;
 
-  const uint16_t* xrow = X + (size_t)(valid ? m : 0) * ldx;
-  for (int g = wave; g < G; g += QA_WAVES) {
-    const int k0 = g * W4A4_GROUP + kc * 16;
+  // ---- 1. 1/λ and L1 rows of the slice -> LDS. Slot s (16 B) of the block's LDS: s < 16 ng are
+  // 1/λ; then rank row c uses slots [16 ng + c (8 ng + 1), +8 ng + 1) for k = 64 g0 .. 64 (g0 + ng),
+  // the last one padding. Each DMA instruction fills 64 consecutive slots.
+  const int n_il = ng * 16, l1_row = ng * 8 + 1, n_all = n_il + RP * l1_row;
+  for (int s0 = wave * 64; s0 < n_all; s0 += QA_WAVES * 64) {
+    const int s = s0 + lane;
+    const void* src = inv_lambda + (size_t)g0 * W4A4_GROUP + 4 * min(s, n_il - 1);
+    if (NT > 0 && s >= n_il && s < n_all) {
+      const int c = (s - n_il) / l1_row, j = (s - n_il) % l1_row;
+      src = l1t + (size_t)c * K + (size_t)g0 * W4A4_GROUP + 8 * (j < ng * 8 ? j : 0);
+    }
+    __builtin_amdgcn_global_load_lds(src, smem + 16 * s0, 16, 0, 0);
+  }
+
+  // ---- 2. X of every group of the slice, straight into registers: exactly 2 * QA_MAX_GS loads
+  // per wave after the DMA, unconditional (rows past M read row M-1 and are zeroed at use, groups
+  // past the slice reload its last group), so vmcnt(2 QA_MAX_GS) means the DMA has landed while
+  // the X loads may still be in flight
+  const uint16_t* xrow = X + (size_t)min(row, M - 1) * ldx + (size_t)g0 * W4A4_GROUP + kc * 16;
+  uint4 xv[QA_MAX_GS][2];
+#pragma unroll
+  for (int i = 0; i < QA_MAX_GS; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) xv[i][h] = *reinterpret_cast<const uint4*>(xrow + min(i, ng - 1) * W4A4_GROUP + 8 * h);
+  asm volatile("" ::: "memory");  // the loads stay ahead of the wait that counts them
+  wait_vmcnt<2 * QA_MAX_GS>();
+  __builtin_amdgcn_s_barrier();
+  const float* s_il = reinterpret_cast<const float*>(smem);
+  const uint8_t* s_l1 = smem + 16 * n_il;
+  const int l1_stride = 16 * l1_row;
+
+  constexpr int NTA = NT > 0 ? NT : 1;
+  v4f acc[NTA];
+#pragma unroll
+  for (int c = 0; c < NTA; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int i = 0; i < QA_MAX_GS; ++i) {
+    if (i >= ng) break;  // block-uniform
+    const int g = g0 + i;
+    const float* il = s_il + i * W4A4_GROUP + kc * 16;
     float xh[2][8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint4 xv = valid ? *reinterpret_cast<const uint4*>(xrow + k0 + 8 * h) : make_uint4(0, 0, 0, 0);
-      const float4 i0 = *reinterpret_cast<const float4*>(inv_lambda + k0 + 8 * h);
-      const float4 i1 = *reinterpret_cast<const float4*>(inv_lambda + k0 + 8 * h + 4);
-      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-      const float il[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+      const float4 i0 = *reinterpret_cast<const float4*>(il + 8 * h);
+      const float4 i1 = *reinterpret_cast<const float4*>(il + 8 * h + 4);
+      const uint32_t xw[4] = {valid ? xv[i][h].x : 0u, valid ? xv[i][h].y : 0u, valid ? xv[i][h].z : 0u,
+                              valid ? xv[i][h].w : 0u};
+      const float ilv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t bits = (e & 1) ? (xw[e >> 1] >> 16) : (xw[e >> 1] & 0xFFFFu);
-        xh[h][e] = bf16f(bits) * il[e];  // one fp32 multiply (no contraction: nothing to fuse)
+        xh[h][e] = bf16f(bits) * ilv[e];  // one fp32 multiply (no contraction: nothing to fuse)
       }
     }
-    uint2* qdst = reinterpret_cast<uint2*>(xq + ((size_t)g * m_pad + blockIdx.x * QA_ROWS + r) * 32 + kc * 8);
+    uint2* qdst = reinterpret_cast<uint2*>(xq + ((size_t)g * m_pad + row) * 32 + kc * 8);
     if (FMT == W4A4_FMT_INT4_G64) {
       float amax = 0.f;
 #pragma unroll
@@ -116,21 +180,21 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
       float s = bf16f(bf16_rne(amax / 7.0f));
       if (!(s >= 0x1p-126f)) s = 0.f;
       const float inv = s != 0.f ? 1.0f / s : 0.f;
-      uint32_t img[3] = {0u, 0u, 0u};  // FP6 image of the lane's 16 codes
+      // q = rint(X̂ * (1/s)) (|q| <= 7 by the symmetric scale): the fp32 product is formed as in
+      // the method, and v_cvt_scalef32_2xpk16_fp6_f32 rounds y / 8 to nearest-even on the E2M3
+      // subnormal grid (step 1/8), i.e. emits exactly the carrier field sign|00|rint(y). Its two
+      // sources interleave (field 2e = src0[e], field 2e+1 = src1[e]); fields 16..31 are unused.
+      v16f ev, od;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float y = __builtin_rintf(xh[h][e] * inv);
-          y = fminf(7.f, fmaxf(-7.f, y));
-          const int q = (int)y;
-          const uint32_t fld = (q < 0 ? 32u : 0u) | (uint32_t)(q < 0 ? -q : q);
-          const int bit = 6 * (8 * h + e);  // compile-time after unrolling
-          img[bit >> 5] |= fld << (bit & 31);
-          if ((bit & 31) > 26) img[(bit >> 5) + 1] |= fld >> (32 - (bit & 31));
-        }
-      *qdst = fold_fp6(img[0], img[1], img[2]);
-      if (kc == 0) static_cast<uint16_t*>(xscale)[(size_t)g * m_pad + blockIdx.x * QA_ROWS + r] = (uint16_t)bf16_rne(s);
+      for (int e = 0; e < 8; ++e) {
+        ev[e] = xh[e >> 2][2 * (e & 3)] * inv;
+        od[e] = xh[e >> 2][2 * (e & 3) + 1] * inv;
+        ev[8 + e] = 0.f;
+        od[8 + e] = 0.f;
+      }
+      const v6i img = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
+      *qdst = fold_fp6((uint32_t)img[0], (uint32_t)img[1], (uint32_t)img[2]);
+      if (kc == 0) static_cast<uint16_t*>(xscale)[(size_t)g * m_pad + row] = (uint16_t)bf16_rne(s);
     } else {
       // the lane's 16 values lie in 32-block kc / 2, shared with lane kc ^ 1
       float amax = 0.f;
@@ -148,51 +212,72 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
         e8 = mant <= 0.75f ? ex - 3 : ex - 2;
         e8 = max(-127, min(127, e8));
       }
+      // E2M1 nearest-even of X̂ * 2^-e (exact scaling), sign kept for values that round to
+      // zero: v_cvt_scalef32_pk_fp4_f32 with scale 1 puts codes k, k+1 into byte k/2
       uint32_t word[2] = {0u, 0u};
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        float z[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float y = ldexpf(xh[h][e], -e8);
-          const float a = fabsf(y);
-          const uint32_t idx = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
-                             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
-          const uint32_t nib = ((__float_as_uint(y) >> 28) & 8u) | idx;
-          word[h] |= nib << (4 * e);
-        }
+        for (int e = 0; e < 8; ++e) z[e] = ldexpf(xh[h][e], -e8);
+        word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[0], z[1], 1.0f, 0);
+        word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[2], z[3], 1.0f, 1);
+        word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[4], z[5], 1.0f, 2);
+        word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[6], z[7], 1.0f, 3);
+      }
       *qdst = make_uint2(word[0], word[1]);
       if ((kc & 1) == 0)
-        static_cast<uint8_t*>(xscale)[(size_t)(2 * g + (kc >> 1)) * m_pad + blockIdx.x * QA_ROWS + r] = (uint8_t)(e8 + 127);
+        static_cast<uint8_t*>(xscale)[(size_t)(2 * g + (kc >> 1)) * m_pad + row] = (uint8_t)(e8 + 127);
     }
     if (NT > 0) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         v4i a;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) a[d] = (int)(bf16_rne(xh[h][2 * d]) | (bf16_rne(xh[h][2 * d + 1]) << 16));
+        for (int d = 0; d < 4; ++d) a[d] = (int)pack_bf16x2(xh[h][2 * d], xh[h][2 * d + 1]);
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-          const v4i b = *reinterpret_cast<const v4i*>(l1t + (size_t)(c * 16 + r) * K + k0 + 8 * h);
+          const v4i b = *reinterpret_cast<const v4i*>(s_l1 + (c * 16 + r) * l1_stride + i * 128 + kc * 32 + 16 * h);
           acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc[c], 0, 0, 0);
         }
       }
     }
   }
   if (NT > 0) {
-    constexpr int RP = NT * 16;
-    // 16x16 MFMA output: lane holds column lane%16, rows 4*(lane/16) + v
+    // 16x16 MFMA output: lane holds rank column c*16 + lane%16, rows 4*(lane/16) + v of the tile
+    const size_t n = (size_t)m_pad * RP;
+    float* dst = xl1 + (nsl > 1 ? n * (1 + sl) : 0) + ((size_t)rb * QA_BLOCK_ROWS + wave * 16) * RP;
 #pragma unroll
     for (int c = 0; c < NT; ++c)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s_part[(wave * QA_ROWS + 4 * kc + v) * RP + c * 16 + r] = acc[c][v];
-    __syncthreads();
-    for (int i = threadIdx.x; i < QA_ROWS * RP; i += QA_WAVES * 64) {
-      float t = 0.f;
-#pragma unroll
-      for (int w = 0; w < QA_WAVES; ++w) t += s_part[w * QA_ROWS * RP + i];
-      xl1[(size_t)blockIdx.x * QA_ROWS * RP + i] = t;
-    }
+      for (int v = 0; v < 4; ++v) dst[(4 * kc + v) * RP + c * 16 + r] = acc[c][v];
   }
+}
+
+// t = Σ_slices partial t, summed in slice order (deterministic); n = m_pad * rank_pad floats.
+// One float4 per thread; the loads of four planes are issued together.
+__global__ __launch_bounds__(256) void t_reduce_kernel(const float* __restrict__ part, int nsl, int n,
+                                                       float* __restrict__ t) {
+  const int i = 4 * (blockIdx.x * 256 + threadIdx.x);
+  if (i >= n) return;
+  auto ld = [&](int k) { return *reinterpret_cast<const float4*>(part + (size_t)k * n + i); };
+  auto add = [](float4& s, const float4& v) {
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  };
+  float4 s = ld(0);
+  int k = 1;
+  for (; k + 3 < nsl; k += 4) {
+    const float4 a = ld(k), b = ld(k + 1), c = ld(k + 2), d = ld(k + 3);
+    add(s, a);
+    add(s, b);
+    add(s, c);
+    add(s, d);
+  }
+  for (; k < nsl; ++k) add(s, ld(k));
+  *reinterpret_cast<float4*>(t + i) = s;
 }
 
 // ===================================================================================
@@ -237,13 +322,6 @@ struct I4Slot {
   uint8_t b[256 * 32];
   uint16_t s[512];
 };
-
-// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left alone), visible to the compiler's wait tracking
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
 
 template <int NTR>  // NTR = rank_pad / 16
 __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
@@ -564,9 +642,19 @@ __global__ __launch_bounds__(G_THREADS) void gemm_mxfp4_kernel(
 template <int FMT, int NT>
 hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, const uint16_t* l1t, int m_pad,
                      uint8_t* xq, void* xs, float* xl1, hipStream_t st) {
-  const size_t lds = NT > 0 ? sizeof(float) * QA_WAVES * QA_ROWS * NT * 16 : 0;
-  hipLaunchKernelGGL((quantize_act_kernel<FMT, NT>), dim3(m_pad / QA_ROWS), dim3(QA_WAVES * 64), lds, st, X, M, K,
-                     ldx, il, l1t, m_pad, xq, xs, xl1);
+  const int gs = qa_group_slice(M, K), nsl = qa_slices(M, K);
+  const size_t lds = 16 * (size_t)qa_lds_slots(NT * 16, gs);
+  if (lds > 65536) {  // large ranks: allow the block more than 64 KB of dynamic LDS
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&quantize_act_kernel<FMT, NT>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL((quantize_act_kernel<FMT, NT>), dim3(m_pad / QA_BLOCK_ROWS * nsl), dim3(QA_WAVES * 64), lds, st,
+                     X, M, K, ldx, il, l1t, m_pad, gs, xq, xs, xl1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || NT == 0 || nsl == 1) return e;
+  const int n = m_pad * NT * 16;
+  hipLaunchKernelGGL(t_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, xl1 + n, nsl, n, xl1);
   return hipGetLastError();
 }
 

@@ -375,7 +375,7 @@ w4a4_status_t w4a4_buffer_sizes(int M, int N, int K, int rank, int fmt, w4a4_siz
   out->l2t = np * rp * 2;
   out->xq = mp * kk / 2;
   out->xscale = mx ? (kk / W4A4_MX_BLOCK) * mp : (kk / W4A4_GROUP) * mp * 2;
-  out->xl1 = mp * rp * 4;
+  out->xl1 = xl1_floats(M, K, rank) * 4;
   return W4A4_OK;
 }
 

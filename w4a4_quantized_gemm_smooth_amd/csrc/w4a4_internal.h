@@ -26,6 +26,32 @@ inline w4a4_status_t check_shape(int M, int N, int K, int rank, int fmt) {
   return W4A4_OK;
 }
 
+// Activation kernel blocking: 128 rows x a slice of at most QA_MAX_GS groups per block, so the
+// slice's L1 rows are fetched once per 128 rows. With several slices each block writes the
+// partial t of its slice to a scratch plane behind t, and a second kernel sums the planes in slice
+// order (deterministic). Cross-block reduction inside one kernel would need device-scope release
+// fences, which write back the per-XCD L2s.
+constexpr int QA_BLOCK_ROWS = 128, QA_MAX_GS = 8;
+constexpr int QA_TARGET_BLOCKS = 128;  // slices are added until the grid has this many blocks
+inline int qa_group_slice(int M, int K) {  // groups per slice
+  const int rb = rows_pad_of(M) / QA_BLOCK_ROWS, G = K / W4A4_GROUP;
+  int ks = (QA_TARGET_BLOCKS + rb - 1) / rb;
+  if (ks < (G + QA_MAX_GS - 1) / QA_MAX_GS) ks = (G + QA_MAX_GS - 1) / QA_MAX_GS;
+  if (ks > G) ks = G;
+  return (G + ks - 1) / ks;
+}
+inline int qa_slices(int M, int K) {
+  const int gs = qa_group_slice(M, K), G = K / W4A4_GROUP;
+  return (G + gs - 1) / gs;
+}
+// floats of the xl1 buffer: t [m_pad][rank_pad], then [slices][m_pad][rank_pad] partial planes
+// when there is more than one slice
+inline size_t xl1_floats(int M, int K, int rank) {
+  const size_t t = size_t(rows_pad_of(M)) * size_t(rank_pad_of(rank));
+  const int ks = qa_slices(M, K);
+  return rank == 0 ? 0 : (ks > 1 ? t * size_t(1 + ks) : t);
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace w4a4
