@@ -98,6 +98,9 @@ def main():
     ap.add_argument("--workload", default="flux_qkv")
     ap.add_argument("--batch", type=int, default=0, help="rows of X for the mxfp4 sweep (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the run, copy a MIB-sized device buffer 3 times (a plain copy of known size, "
+                         "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's multi-GPU sharding "
@@ -191,6 +194,20 @@ def main():
                      "TOPS_cold": round(ops / (np.mean(cg) * 1e-3) / 1e12, 2)},
         },
     }
+    if args.copy_calibration:
+        n = args.copy_calibration << 18   # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            log(f"[bench] copy {args.copy_calibration} MiB: {ms * 1e3:.1f} us, {2 * n * 4 / ms / 1e6:.0f} GB/s (read+write)")
+        out["copy_calibration_mib"] = args.copy_calibration
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, lam, inv)
     print(json.dumps(out), flush=True)
