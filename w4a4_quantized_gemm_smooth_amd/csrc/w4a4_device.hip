@@ -492,19 +492,54 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
     }
   }
 
-  // store: 32x32 output layout, lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4
+  // store through LDS, so that every lane writes whole 16-byte row segments: the wave's 128 x 64
+  // tile goes out in two halves of 64 rows, staged in the wave's own (now idle) ring slot with a
+  // 144-byte row stride (conflict-free 2-byte writes and 16-byte reads). The 32x32 MFMA output
+  // layout: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4.
+  __builtin_amdgcn_s_barrier();  // every wave is done with the ring (and its DMA has landed)
+  constexpr int ES = 144;
+  uint8_t* stage = reinterpret_cast<uint8_t*>(ring[0]);
+#pragma unroll
+  for (int w = 1; w < I4_NS; ++w)
+    if (wave == w) stage = reinterpret_cast<uint8_t*>(ring[w]);  // wave-uniform select
+  static_assert(64 * ES <= (int)sizeof(I4Slot), "staging fits a ring slot");
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(Y) & 15u) == 0) && (ldy % 8 == 0);
+  float bcol[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = n0 + wn * 64 + j * 32 + lr;
-    if (col >= N) continue;
-    const float bcol = bias ? bf16f(bias[col]) : 0.f;
+    bcol[j] = (bias && col < N) ? bf16f(bias[col]) : 0.f;
+  }
 #pragma unroll
-    for (int i = 0; i < I4_MT; ++i)
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        if (row < M) Y[(size_t)row * ldy + col] = (uint16_t)bf16_rne(acc[i][j][v] + bcol);
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const int rl = ii * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+          const uint32_t pr = pack_bf16x2(acc[2 * half + ii][j][v] + bcol[j], acc[2 * half + ii][j][v + 1] + bcol[j]);
+          uint16_t* d = reinterpret_cast<uint16_t*>(stage + rl * ES + (j * 32 + lr) * 2);
+          d[0] = (uint16_t)pr;
+          d[ES / 2] = (uint16_t)(pr >> 16);
+        }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = q * 64 + lane, rr = idx >> 3, c = idx & 7;
+      const uint4 val = *reinterpret_cast<const uint4*>(stage + rr * ES + c * 16);
+      const int row = m0 + wm * 128 + half * 64 + rr, col = n0 + wn * 64 + c * 8;
+      if (row >= M) continue;
+      uint16_t* dst = Y + (size_t)row * ldy + col;
+      if (vec_ok && col + 8 <= N) {
+        *reinterpret_cast<uint4*>(dst) = val;
+      } else {
+        const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
       }
+    }
   }
 }
 
