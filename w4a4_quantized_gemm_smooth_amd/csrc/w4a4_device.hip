@@ -430,13 +430,8 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
       for (int t = 0; t < T; ++t) {
         const int i = t >> 1, j = t & 1;
         const int t1 = t + 1, i1 = (t1 % T) >> 1, j1 = t1 & 1;
-        if (t1 == T - 2) {  // next group's B operands and scales
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            Bn_raw[jj] = b_raw(nxt, jj);
-            OBn[jj] = sc_val(nxt, 256 + bcol0 + 32 * jj, live1);
-          }
-        }
+        // consume the operands read two tiles ago first, then issue the next reads, so that the
+        // wait for the old reads never has to cover the new ones
         if (t1 == T) {  // switch to group g + 1
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
@@ -444,9 +439,12 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
             OB[jj] = OBn[jj];
           }
         }
-        if (j1 == 0) {  // new tile row: take the prefetched A operand, prefetch the following one
+        if (j1 == 0) {  // new tile row: take the prefetched A operand
           Av = unfold_fp6(An_raw);
           OA = OAn;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (j1 == 0) {  // prefetch the following row's A operand
           if (t1 < T - 2) {
             An_raw = a_raw(cur, i1 + 1);
             OAn = sc_val(cur, arow0 + 32 * (i1 + 1), live0);
@@ -456,6 +454,14 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
             OAn = sc_val(nxt, arow0 + 32 * r1, live1);
           }
         }
+        if (t1 == T - 2) {  // next group's B operands and scales
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            Bn_raw[jj] = b_raw(nxt, jj);
+            OBn[jj] = sc_val(nxt, 256 + bcol0 + 32 * jj, live1);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch reads here, two tiles ahead of their use
         const v16f pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[j1], zero16, 2, 2, 0, 130, 0, 130);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
