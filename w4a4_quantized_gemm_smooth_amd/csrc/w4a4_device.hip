@@ -281,15 +281,18 @@ __global__ __launch_bounds__(256) void t_reduce_kernel(const float* __restrict__
 }
 
 // ===================================================================================
-// Kernel 2: INT4 GEMM + group-scale epilogue + low-rank up projection (+ bias), bf16 out.
+// Kernel 2: the 4-bit GEMM + low-rank up projection (+ bias), bf16 out, INT4 or MXFP4.
 //
 // Block tile 256 (M) x 256 (N), 8 waves as 2 (M) x 4 (N); each wave owns a 4 x 2 grid of 32x32
-// tiles. One K step = one 64-wide group. The folded codes and the bf16 scales of each group are
-// copied global -> LDS by the LDS DMA path (global_load_lds) into a ring of I4_NS slots, issued
-// four groups before their first reader; one barrier per two groups publishes the next slots
-// slot. Per group each wave unfolds its A and B operands to FP6 and runs, per tile, one FP6 MFMA
-// with E8M0 scales 2^3 x 2^3 (the exact integer dot product of the group), one bf16 MFMA (the
-// exact outer product s_x s_w of the raw bf16 scales) and 16 FMAs into its fp32 accumulators.
+// tiles. One K step = one 64-wide group. The codes and scales of each group are copied global ->
+// LDS by the LDS DMA path (global_load_lds) into a ring of I4_NS slots, issued four groups before
+// their first reader; one barrier per two groups publishes the next slots.
+//  * INT4: per group each wave unfolds its A and B operands to FP6 and runs, per tile, one FP6 MFMA
+//    with E8M0 scales 2^3 x 2^3 (the exact integer dot product of the group), one bf16 MFMA (the
+//    exact outer product s_x s_w of the raw bf16 scales) and 16 FMAs into its fp32 accumulators.
+//  * MXFP4: one FP4 MFMA per tile with the E8M0 block scales as its operand scales, accumulating
+//    in place.
+// The epilogue adds bf16(t)·L2 and the bias and writes Y through LDS in 16-byte row segments.
 // ===================================================================================
 constexpr int I4_BM = 256, I4_BN = 256, I4_THREADS = 512;
 constexpr int I4_MT = 4;            // 32-row tiles per wave (M)
@@ -323,12 +326,13 @@ struct I4Slot {
   uint16_t s[512];
 };
 
-template <int NTR>  // NTR = rank_pad / 16
-__global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
-    const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs, const float* __restrict__ xl1,
-    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
+template <int FMT, int NTR>  // NTR = rank_pad / 16
+__global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ xl1,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
     int m_pad, int n_pad) {
+  constexpr bool INT4 = FMT == W4A4_FMT_INT4_G64;
   __shared__ __attribute__((aligned(16))) I4Slot sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7;
   I4Slot* const ring[I4_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5, &sl6, &sl7};
 
@@ -342,24 +346,39 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
 
   // ---- DMA sources. Instruction w of an operand fills LDS bytes [1024 w, 1024 w + 1024) of the
   // slot, lane i the 16 bytes at 1024 w + 16 i = row 32 w + i / 2, stored half i & 1; the lane
-  // loads the global half that the swizzle puts there. Scales: wave w copies 128 scales (256 B)
-  // of block w & 3 (A rows, then B rows); waves w and w + 4 write the same bytes.
+  // loads the global half that the swizzle puts there. Scales: wave w copies 256 bytes, chunk
+  // w & 3 of the slot's 1 KB of scales; waves w and w + 4 write the same bytes. INT4: bf16 scales
+  // of A rows 0..127, A rows 128..255, B rows 0..127, B rows 128..255. MXFP4: E8M0 bytes of A block
+  // 2g, A block 2g+1, B block 2g, B block 2g+1 (256 rows each).
   const int drow = 32 * wave + (lane >> 1);
   const int dhalf = (lane & 1) ^ ((drow >> 3) & 1);
-  const uint32_t c_lane = drow * 32 + 16 * dhalf;   // byte offset of the lane's 16 B in a code tile
+  const int c_lane = drow * 32 + 16 * dhalf;   // byte offset of the lane's 16 B in a code tile
   const int sblk = wave & 3;
-  const uint32_t s_lane = 4 * lane;                  // byte offset of the lane's two scales
-  // 3 vector-memory instructions per wave and group (uniform base + 32-bit lane offset); groups
-  // past the end reload the last group
+  const int s_lane = 4 * lane;                 // byte offset of the lane's 4 bytes of scales
+  // Buffer resources (scalar base + bounds) per operand: the lane offsets stay in one VGPR each and
+  // the group offset is a scalar soffset. Loads past a buffer's end would return zeros.
+  constexpr int RSRC_W3 = 0x00020000;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(xq + (size_t)m0 * 32), 0, (G * m_pad - m0) * 32, RSRC_W3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wq + (size_t)n0 * 32), 0, (G * n_pad - n0) * 32, RSRC_W3);
+  // scale chunk of this wave: INT4 bf16 rows [128 c, 128 c + 128) of A (c = sblk) or B (c = sblk - 2);
+  // MXFP4 E8M0 plane (2g + c) of A or B, 256 rows
+  const bool s_is_a = sblk < 2;
+  const int s_rows = s_is_a ? m_pad : n_pad, s_row0 = s_is_a ? m0 : n0, sc_ = s_is_a ? sblk : sblk - 2;
+  const uint8_t* s_buf = s_is_a ? xs : ws;
+  const int s_first = INT4 ? 2 * (s_row0 + 128 * sc_) : sc_ * s_rows + s_row0;           // bytes
+  const int s_gstride = 2 * s_rows;  // bytes per group: one bf16 per row, or two E8M0 planes
+  const int s_total = G * s_gstride;
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(s_buf + s_first), 0, s_total - s_first, RSRC_W3);
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  // 3 vector-memory instructions per wave and group; groups past the end reload the last group
   auto dma = [&](int g, I4Slot* sl) {
     g = min(g, G - 1);
-    const uint8_t* a_base = xq + ((size_t)g * m_pad + m0) * 32;
-    const uint8_t* b_base = wq + ((size_t)g * n_pad + n0) * 32;
-    const uint8_t* s_base = sblk < 2 ? reinterpret_cast<const uint8_t*>(xs + (size_t)g * m_pad + m0 + 128 * sblk)
-                                     : reinterpret_cast<const uint8_t*>(ws + (size_t)g * n_pad + n0 + 128 * (sblk - 2));
-    __builtin_amdgcn_global_load_lds(a_base + c_lane, sl->a + 1024 * wave, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(b_base + c_lane, sl->b + 1024 * wave, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(s_base + s_lane, sl->s + 128 * sblk, 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr)(sl->a + 1024 * wave), 16, c_lane, g * m_pad * 32, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr)(sl->b + 1024 * wave), 16, c_lane, g * n_pad * 32, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr)(sl->s + 128 * sblk), 4, s_lane, g * s_gstride, 0, 0);
   };
 
   v16f acc[I4_MT][2];
@@ -375,6 +394,14 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
   // operand byte offsets inside a slot (tile i / j adds 1024 i / 1024 j)
   const int a_off = sw_off32(arow0, lh), b_off = sw_off32(bcol0, lh);
 
+  // prologue: groups 0 .. NS-3 in flight; group 0 visible
+#pragma unroll
+  for (int s = 0; s < I4_NS - 2; ++s) dma(s, ring[s]);
+  wait_vmcnt<3 * (I4_NS - 3)>();
+  __builtin_amdgcn_s_barrier();
+  auto a_raw = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i); };
+  auto b_raw = [&](const I4Slot* sl, int j) { return *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j); };
+  if constexpr (INT4) {
   // operands of the scale outer product: bf16 scale at k = 0 (lanes 0..31), zero elsewhere;
   // groups past the end get zero scales. Kept as one register, widened at the MFMA.
   auto sc_val = [&](const I4Slot* sl, int row, bool live) -> uint32_t {
@@ -382,14 +409,8 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
     return (lh == 0 && live) ? s : 0u;
   };
   auto sc_op = [](uint32_t s) { return v4s{(short)s, 0, 0, 0}; };
-  auto a_raw = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i); };
-  auto b_raw = [&](const I4Slot* sl, int j) { return *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j); };
 
-  // prologue: groups 0 .. NS-3 in flight; group 0 visible; its first operands in registers
-#pragma unroll
-  for (int s = 0; s < I4_NS - 2; ++s) dma(s, ring[s]);
-  wait_vmcnt<3 * (I4_NS - 3)>();
-  __builtin_amdgcn_s_barrier();
+  // its first operands in registers
   v8i Bv[2], Av;
   uint32_t OB[2], OA;
   v4i An_raw, Bn_raw[2];
@@ -472,6 +493,85 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
       }
     }
   }
+  } else {
+    // ---- MXFP4: E2M1 x E2M1 with the E8M0 block scales applied by the MFMA (lane half h of a row
+    // is K block 2g + h), accumulating in place; no group epilogue. Operands are read two tiles
+    // ahead (A rows) and four tiles ahead (the next group's B), as in the INT4 loop.
+    // Groups past the end read their (stale) slot with A forced to +0 codes: they add exactly 0.
+    auto sa_val = [&](const I4Slot* sl, int i) {
+      return (int)reinterpret_cast<const uint8_t*>(sl->s)[256 * lh + arow0 + 32 * i];
+    };
+    auto sb_val = [&](const I4Slot* sl, int j) {
+      return (int)reinterpret_cast<const uint8_t*>(sl->s)[512 + 256 * lh + bcol0 + 32 * j];
+    };
+    auto a_live = [&](const I4Slot* sl, int i, bool live) {
+      const v4i a = a_raw(sl, i);
+      return live ? a : v4i{0, 0, 0, 0};
+    };
+    auto op8 = [](v4i v) { return v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0}; };
+    v4i Av, An, Bv[2], Bn[2];
+    int sAv, sAn, sBv[2], sBn[2];
+    Av = a_raw(ring[0], 0);
+    sAv = sa_val(ring[0], 0);
+    An = a_raw(ring[0], 1);
+    sAn = sa_val(ring[0], 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      Bv[j] = b_raw(ring[0], j);
+      sBv[j] = sb_val(ring[0], j);
+    }
+    constexpr int T = 2 * I4_MT;
+    for (int g0 = 0; g0 < G; g0 += I4_NS) {
+#pragma unroll
+      for (int u = 0; u < I4_NS; ++u) {
+        const int g = g0 + u;
+        const I4Slot* cur = ring[u];
+        const I4Slot* nxt = ring[(u + 1) % I4_NS];
+        if (u % 2 == 0) {
+          wait_vmcnt<3 * (I4_NS - 5)>();
+          __builtin_amdgcn_s_barrier();
+          dma(g + I4_NS - 2, ring[(u + I4_NS - 2) % I4_NS]);
+          dma(g + I4_NS - 1, ring[(u + I4_NS - 1) % I4_NS]);
+        }
+        const bool live0 = g < G, live1 = g + 1 < G;
+        asm volatile("" ::: "memory");  // LDS reads of this group stay inside its step
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const int i = t >> 1, j = t & 1;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8(Av), op8(Bv[j]), acc[i][j], 4, 4, 0, sAv, 0, sBv[j]);
+          __builtin_amdgcn_sched_barrier(0);
+          const int t1 = t + 1, i1 = (t1 % T) >> 1, j1 = t1 & 1;
+          if (t1 == T) {  // switch to group g + 1
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              Bv[jj] = Bn[jj];
+              sBv[jj] = sBn[jj];
+            }
+          }
+          if (j1 == 0) {  // next row: take the prefetched A, read the following one
+            Av = An;
+            sAv = sAn;
+            if (t1 < T - 2) {
+              An = a_live(cur, i1 + 1, live0);
+              sAn = sa_val(cur, i1 + 1);
+            } else {
+              const int r1 = t1 == T - 2 ? 0 : 1;
+              An = a_live(nxt, r1, live1);
+              sAn = sa_val(nxt, r1);
+            }
+          }
+          if (t1 == T - 4) {  // the next group's B operands
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              Bn[jj] = b_raw(nxt, jj);
+              sBn[jj] = sb_val(nxt, jj);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
   wait_vmcnt<0>();  // no LDS DMA may outlive the block
 
   // low-rank up projection: acc += bf16(t) · L2 over k = rank index (32x32x16 bf16 MFMA)
@@ -549,136 +649,6 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_int4_kernel(
   }
 }
 
-// ===================================================================================
-// MXFP4 tiling (kernel 3): block 128 x 128, 2 x 2 waves of 64 x 64.
-// ===================================================================================
-constexpr int GB_M = 128, GB_N = 128, G_THREADS = 256;
-
-// ===================================================================================
-// Kernel 3: MXFP4 GEMM (E2M1 x E2M1 with E8M0 block scales applied by the MFMA) + low-rank
-// epilogue. Same tiling as kernel 2; one K step = 64 = two 32-blocks (lanes 0-31 / 32-63).
-// ===================================================================================
-template <int NTR>
-__global__ __launch_bounds__(G_THREADS) void gemm_mxfp4_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ xl1,
-    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
-    int m_pad, int n_pad) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][GB_M * 32];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][GB_N * 32];
-  __shared__ uint8_t s_sa[2][2][GB_M];
-  __shared__ uint8_t s_sb[2][2][GB_N];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_m = m_pad / GB_M;
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int m0 = tm * GB_M, n0 = tn * GB_N;
-  const int G = K / W4A4_GROUP;
-
-  const int lrow = tid >> 1, lhalf = tid & 1;
-  const uint8_t* a_src = xq + ((size_t)(m0 + lrow)) * 32 + lhalf * 16;
-  const uint8_t* b_src = wq + ((size_t)(n0 + lrow)) * 32 + lhalf * 16;
-  const size_t a_gstride = (size_t)m_pad * 32, b_gstride = (size_t)n_pad * 32;
-
-  uint4 ra, rb;
-  uint32_t rs = 0;
-  // scales: 2 blocks x 128 rows = 256 bytes per operand; threads 0..63 -> A, 64..127 -> B (4 B each)
-  auto gload = [&](int g) {
-    ra = *reinterpret_cast<const uint4*>(a_src + g * a_gstride);
-    rb = *reinterpret_cast<const uint4*>(b_src + g * b_gstride);
-    if (tid < 64) {
-      const int blk = tid >> 5, rr = (tid & 31) * 4;
-      rs = *reinterpret_cast<const uint32_t*>(xs + (size_t)(2 * g + blk) * m_pad + m0 + rr);
-    } else if (tid < 128) {
-      const int t2 = tid - 64, blk = t2 >> 5, rr = (t2 & 31) * 4;
-      rs = *reinterpret_cast<const uint32_t*>(ws + (size_t)(2 * g + blk) * n_pad + n0 + rr);
-    }
-  };
-  auto lstore = [&](int buf) {
-    *reinterpret_cast<uint4*>(&s_a[buf][sw_off32(lrow, lhalf)]) = ra;
-    *reinterpret_cast<uint4*>(&s_b[buf][sw_off32(lrow, lhalf)]) = rb;
-    if (tid < 64) *reinterpret_cast<uint32_t*>(&s_sa[buf][tid >> 5][(tid & 31) * 4]) = rs;
-    else if (tid < 128) *reinterpret_cast<uint32_t*>(&s_sb[buf][(tid - 64) >> 5][((tid - 64) & 31) * 4]) = rs;
-  };
-
-  v16f acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  const int lr = lane & 31, lh = lane >> 5;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    if (g + 1 < G) gload(g + 1);
-    v8i A[2], B[2];
-    int SA[2], SB[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = wm * 64 + i * 32 + lr;
-      const v4i v = *reinterpret_cast<const v4i*>(&s_a[buf][sw_off32(row, lh)]);
-      A[i] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-      SA[i] = s_sa[buf][lh][row];
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = wn * 64 + j * 32 + lr;
-      const v4i v = *reinterpret_cast<const v4i*>(&s_b[buf][sw_off32(col, lh)]);
-      B[j] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-      SB[j] = s_sb[buf][lh][col];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[i], B[j], acc[i][j], 4, 4, 0, SA[i], 0, SB[j]);
-    if (g + 1 < G) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  if (NTR > 0) {
-    constexpr int RP = NTR * 16;
-#pragma unroll
-    for (int kk = 0; kk < RP; kk += 16) {
-      v4i TA[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const float* tp = xl1 + (size_t)(m0 + wm * 64 + i * 32 + lr) * RP + kk + 8 * lh;
-        const float4 t0 = *reinterpret_cast<const float4*>(tp);
-        const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
-        TA[i] = v4i{(int)(bf16_rne(t0.x) | (bf16_rne(t0.y) << 16)), (int)(bf16_rne(t0.z) | (bf16_rne(t0.w) << 16)),
-                    (int)(bf16_rne(t1.x) | (bf16_rne(t1.y) << 16)), (int)(bf16_rne(t1.z) | (bf16_rne(t1.w) << 16))};
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const v4i lb = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 64 + j * 32 + lr) * RP + kk + 8 * lh);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(TA[i]), as_bf16x8(lb), acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + wn * 64 + j * 32 + lr;
-    if (col >= N) continue;
-    const float bcol = bias ? bf16f(bias[col]) : 0.f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        if (row < M) Y[(size_t)row * ldy + col] = (uint16_t)bf16_rne(acc[i][j][v] + bcol);
-      }
-  }
-}
-
 // ----------------------------------------------------------------------------- launch helpers
 template <int FMT, int NT>
 hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, const uint16_t* l1t, int m_pad,
@@ -716,12 +686,15 @@ template <int NTR>
 hipError_t launch_gemm(int fmt, const uint8_t* xq, const void* xs, const float* xl1, const uint8_t* wq,
                        const void* ws, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy, int M,
                        int N, int K, int m_pad, int n_pad, hipStream_t st) {
+  const dim3 grid((m_pad / I4_BM) * (n_pad / I4_BN)), block(I4_THREADS);
+  const uint8_t* xsb = static_cast<const uint8_t*>(xs);
+  const uint8_t* wsb = static_cast<const uint8_t*>(ws);
   if (fmt == W4A4_FMT_INT4_G64)
-    hipLaunchKernelGGL((gemm_int4_kernel<NTR>), dim3((m_pad / I4_BM) * (n_pad / I4_BN)), dim3(I4_THREADS), 0, st, xq, static_cast<const uint16_t*>(xs),
-                       xl1, wq, static_cast<const uint16_t*>(ws), l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
+    hipLaunchKernelGGL((gemm_kernel<W4A4_FMT_INT4_G64, NTR>), grid, block, 0, st, xq, xsb, xl1, wq, wsb, l2t, bias, Y,
+                       ldy, M, N, K, m_pad, n_pad);
   else
-    hipLaunchKernelGGL((gemm_mxfp4_kernel<NTR>), dim3((m_pad / GB_M) * (n_pad / GB_N)), dim3(G_THREADS), 0, st, xq, static_cast<const uint8_t*>(xs),
-                       xl1, wq, static_cast<const uint8_t*>(ws), l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
+    hipLaunchKernelGGL((gemm_kernel<W4A4_FMT_MXFP4_B32, NTR>), grid, block, 0, st, xq, xsb, xl1, wq, wsb, l2t, bias,
+                       Y, ldy, M, N, K, m_pad, n_pad);
   return hipGetLastError();
 }
 
