@@ -495,80 +495,47 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   }
   } else {
     // ---- MXFP4: E2M1 x E2M1 with the E8M0 block scales applied by the MFMA (lane half h of a row
-    // is K block 2g + h), accumulating in place; no group epilogue. Operands are read two tiles
-    // ahead (A rows) and four tiles ahead (the next group's B), as in the INT4 loop.
+    // is K block 2g + h), accumulating in place; no group epilogue. All operands of group g + 1 are
+    // read from LDS at the start of group g (double-buffered registers), a whole group ahead.
     // Groups past the end read their (stale) slot with A forced to +0 codes: they add exactly 0.
-    auto sa_val = [&](const I4Slot* sl, int i) {
-      return (int)reinterpret_cast<const uint8_t*>(sl->s)[256 * lh + arow0 + 32 * i];
-    };
-    auto sb_val = [&](const I4Slot* sl, int j) {
-      return (int)reinterpret_cast<const uint8_t*>(sl->s)[512 + 256 * lh + bcol0 + 32 * j];
-    };
-    auto a_live = [&](const I4Slot* sl, int i, bool live) {
-      const v4i a = a_raw(sl, i);
-      return live ? a : v4i{0, 0, 0, 0};
+    auto rd = [&](const I4Slot* sl, bool live, v4i (&A)[I4_MT], v4i (&B)[2], int (&sA)[I4_MT], int (&sB)[2]) {
+      const uint8_t* sc = reinterpret_cast<const uint8_t*>(sl->s);
+#pragma unroll
+      for (int i = 0; i < I4_MT; ++i) {
+        const v4i a = a_raw(sl, i);
+        A[i] = live ? a : v4i{0, 0, 0, 0};
+        sA[i] = sc[256 * lh + arow0 + 32 * i];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        B[j] = b_raw(sl, j);
+        sB[j] = sc[512 + 256 * lh + bcol0 + 32 * j];
+      }
     };
     auto op8 = [](v4i v) { return v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0}; };
-    v4i Av, An, Bv[2], Bn[2];
-    int sAv, sAn, sBv[2], sBn[2];
-    Av = a_raw(ring[0], 0);
-    sAv = sa_val(ring[0], 0);
-    An = a_raw(ring[0], 1);
-    sAn = sa_val(ring[0], 1);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      Bv[j] = b_raw(ring[0], j);
-      sBv[j] = sb_val(ring[0], j);
-    }
-    constexpr int T = 2 * I4_MT;
+    v4i A[2][I4_MT], B[2][2];
+    int sA[2][I4_MT], sB[2][2];
+    rd(ring[0], true, A[0], B[0], sA[0], sB[0]);
     for (int g0 = 0; g0 < G; g0 += I4_NS) {
 #pragma unroll
       for (int u = 0; u < I4_NS; ++u) {
-        const int g = g0 + u;
-        const I4Slot* cur = ring[u];
-        const I4Slot* nxt = ring[(u + 1) % I4_NS];
+        const int g = g0 + u, c = u & 1;
         if (u % 2 == 0) {
           wait_vmcnt<3 * (I4_NS - 5)>();
           __builtin_amdgcn_s_barrier();
           dma(g + I4_NS - 2, ring[(u + I4_NS - 2) % I4_NS]);
           dma(g + I4_NS - 1, ring[(u + I4_NS - 1) % I4_NS]);
         }
-        const bool live0 = g < G, live1 = g + 1 < G;
-        asm volatile("" ::: "memory");  // LDS reads of this group stay inside its step
+        __builtin_amdgcn_sched_barrier(0);
+        rd(ring[(u + 1) % I4_NS], g + 1 < G, A[c ^ 1], B[c ^ 1], sA[c ^ 1], sB[c ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);  // the next group's reads stay ahead of this group's MFMAs
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
+        for (int t = 0; t < 2 * I4_MT; ++t) {
           const int i = t >> 1, j = t & 1;
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8(Av), op8(Bv[j]), acc[i][j], 4, 4, 0, sAv, 0, sBv[j]);
-          __builtin_amdgcn_sched_barrier(0);
-          const int t1 = t + 1, i1 = (t1 % T) >> 1, j1 = t1 & 1;
-          if (t1 == T) {  // switch to group g + 1
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-              Bv[jj] = Bn[jj];
-              sBv[jj] = sBn[jj];
-            }
-          }
-          if (j1 == 0) {  // next row: take the prefetched A, read the following one
-            Av = An;
-            sAv = sAn;
-            if (t1 < T - 2) {
-              An = a_live(cur, i1 + 1, live0);
-              sAn = sa_val(cur, i1 + 1);
-            } else {
-              const int r1 = t1 == T - 2 ? 0 : 1;
-              An = a_live(nxt, r1, live1);
-              sAn = sa_val(nxt, r1);
-            }
-          }
-          if (t1 == T - 4) {  // the next group's B operands
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-              Bn[jj] = b_raw(nxt, jj);
-              sBn[jj] = sb_val(nxt, jj);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8(A[c][i]), op8(B[c][j]), acc[i][j], 4, 4, 0,
+                                                                    sA[c][i], 0, sB[c][j]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
