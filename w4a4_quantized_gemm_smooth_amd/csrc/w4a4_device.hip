@@ -324,6 +324,7 @@ struct I4Slot {
   uint8_t a[256 * 32];
   uint8_t b[256 * 32];
   uint16_t s[512];
+  uint16_t z[32];  // zeros (never written by the DMA): k > 0 half of the scale outer-product operand
 };
 
 template <int FMT, int NTR>  // NTR = rank_pad / 16
@@ -394,7 +395,11 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   // operand byte offsets inside a slot (tile i / j adds 1024 i / 1024 j)
   const int a_off = sw_off32(arow0, lh), b_off = sw_off32(bcol0, lh);
 
-  // prologue: groups 0 .. NS-3 in flight; group 0 visible
+  // prologue: zero words of every slot; groups 0 .. NS-3 in flight; group 0 visible
+  if (tid < 32) {
+#pragma unroll
+    for (int s = 0; s < I4_NS; ++s) ring[s]->z[tid] = 0;
+  }
 #pragma unroll
   for (int s = 0; s < I4_NS - 2; ++s) dma(s, ring[s]);
   wait_vmcnt<3 * (I4_NS - 3)>();
@@ -402,13 +407,18 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   auto a_raw = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i); };
   auto b_raw = [&](const I4Slot* sl, int j) { return *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j); };
   if constexpr (INT4) {
-  // operands of the scale outer product: bf16 scale at k = 0 (lanes 0..31), zero elsewhere;
-  // groups past the end get zero scales. Kept as one register, widened at the MFMA.
-  auto sc_val = [&](const I4Slot* sl, int row, bool live) -> uint32_t {
-    const uint32_t s = sl->s[row];
-    return (lh == 0 && live) ? s : 0u;
+  // operands of the scale outer product: the A side is the bf16 scale of the lane's row in every
+  // lane; the B side is the scale at k = 0 (lanes 0..31) and zero for k = 4 (lanes 32..63, read
+  // from the slot's zero words), and zero for groups past the end, so S = s_x s_w exactly. Kept as
+  // one zero-extended register, widened at the MFMA.
+  const int sb_lane_off = lh ? (int)offsetof(I4Slot, z) : (int)offsetof(I4Slot, s) + 2 * (256 + bcol0);
+  auto sa_val = [&](const I4Slot* sl, int row) -> uint32_t { return sl->s[row]; };
+  auto sb_val = [&](const I4Slot* sl, int j, bool live) -> uint32_t {
+    const uint32_t s = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sl) + sb_lane_off + (lh ? 0 : 64 * j));
+    return live ? s : 0u;
   };
-  auto sc_op = [](uint32_t s) { return v4s{(short)s, 0, 0, 0}; };
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  auto sc_op = [](uint32_t s) { return __builtin_bit_cast(v4s, v2u{s, 0u}); };
 
   // its first operands in registers
   v8i Bv[2], Av;
@@ -418,12 +428,12 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     Bv[j] = unfold_fp6(b_raw(ring[0], j));
-    OB[j] = sc_val(ring[0], 256 + bcol0 + 32 * j, true);
+    OB[j] = sb_val(ring[0], j, true);
   }
   Av = unfold_fp6(a_raw(ring[0], 0));
-  OA = sc_val(ring[0], arow0, true);
+  OA = sa_val(ring[0], arow0);
   An_raw = a_raw(ring[0], 1);
-  OAn = sc_val(ring[0], arow0 + 32, true);
+  OAn = sa_val(ring[0], arow0 + 32);
 
   constexpr int T = 2 * I4_MT;
   v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[0], zero16, 2, 2, 0, 130, 0, 130);
@@ -443,7 +453,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
         dma(g + I4_NS - 2, ring[(u + I4_NS - 2) % I4_NS]);
         dma(g + I4_NS - 1, ring[(u + I4_NS - 1) % I4_NS]);
       }
-      const bool live0 = g < G, live1 = g + 1 < G;
+      const bool live1 = g + 1 < G;
       // ---- the group's 8 tiles, software-pipelined: the FP6 MFMA of tile t+1 is issued before the
       // 16 FMAs of tile t and its outer product right after them; the last tile's successor is
       // tile 0 of group g + 1, whose operands are read from the next slot during this group
@@ -468,18 +478,18 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
         if (j1 == 0) {  // prefetch the following row's A operand
           if (t1 < T - 2) {
             An_raw = a_raw(cur, i1 + 1);
-            OAn = sc_val(cur, arow0 + 32 * (i1 + 1), live0);
+            OAn = sa_val(cur, arow0 + 32 * (i1 + 1));
           } else {  // rows 0 and 1 of the next group follow rows 3 and 0
             const int r1 = t1 == T - 2 ? 0 : 1;
             An_raw = a_raw(nxt, r1);
-            OAn = sc_val(nxt, arow0 + 32 * r1, live1);
+            OAn = sa_val(nxt, arow0 + 32 * r1);
           }
         }
         if (t1 == T - 2) {  // next group's B operands and scales
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             Bn_raw[jj] = b_raw(nxt, jj);
-            OBn[jj] = sc_val(nxt, 256 + bcol0 + 32 * jj, live1);
+            OBn[jj] = sb_val(nxt, jj, live1);
           }
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch reads here, two tiles ahead of their use
