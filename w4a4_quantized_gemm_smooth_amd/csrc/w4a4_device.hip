@@ -493,12 +493,18 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
           }
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch reads here, two tiles ahead of their use
+        // raised wave priority around each MFMA issue keeps the matrix pipe fed while the other
+        // wave of the SIMD is in its FMAs
+        __builtin_amdgcn_s_setprio(1);
         const v16f pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[j1], zero16, 2, 2, 0, 130, 0, 130);
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc[v], acc[i][j][v]);
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
         sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sc_op(OA), sc_op(OB[j1]), zero16, 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
         p = pn;
       }
     }
