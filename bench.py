@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--workload", default="flux_qkv")
     ap.add_argument("--batch", type=int, default=0, help="rows of X for the mxfp4 sweep (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the rank-0 (plain W4A4) comparison run")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy a MIB-sized device buffer 3 times (a plain copy of known size, "
                          "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -194,6 +196,25 @@ def main():
                      "TOPS_cold": round(ops / (np.mean(cg) * 1e-3) / 1e12, 2)},
         },
     }
+    if not args.no_ablation and r > 0:
+        # the same layer without the low-rank branch (rank 0: plain W4A4 on the smoothed weight),
+        # to report the branch's overhead (§4.3: fused, it should add only a few percent)
+        prep0 = w4.prepare_weights(d["w"], lam, 0, fmt)
+        layer0 = w4.W4A4Linear(prep0, inv, device=dev)
+        acts0 = layer0.act_buffers(M)
+        for _ in range(args.warmup):
+            layer0.quantize(x)
+            layer0.gemm(acts0, M, y)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            layer0.quantize(x)
+            layer0.gemm(acts0, M, y)
+        torch.cuda.synchronize()
+        ms0 = (time.perf_counter() - t0) * 1e3 / args.steps
+        out["ablation"] = {"rank0_ms_per_step": round(ms0, 5),
+                           "lowrank_overhead_pct": round(100.0 * (ms_step - ms0) / ms0, 2)}
+        del layer0, acts0
     if args.copy_calibration:
         n = args.copy_calibration << 18   # float32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)

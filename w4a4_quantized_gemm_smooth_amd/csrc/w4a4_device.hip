@@ -395,6 +395,113 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   // operand byte offsets inside a slot (tile i / j adds 1024 i / 1024 j)
   const int a_off = sw_off32(arow0, lh), b_off = sw_off32(bcol0, lh);
 
+  // low-rank up projection first: acc = bf16(t) · L2 over k = rank index (32x32x16 bf16 MFMA); the
+  // 4-bit groups then accumulate on top. Up to rank 32 the block's t tile (256 rows x 32 fp32 =
+  // 32 KB, read by four waves each) is copied once into ring slots 6 and 7 by the LDS DMA path
+  // before the ring's first groups, and the L2 operands are loaded before them too; all of it
+  // lands under the prologue's wait for group 0 and the MFMAs run right after it. Larger ranks
+  // load t directly, 32 ranks at a time.
+  constexpr int RP = NTR * 16, KS = 2;  // up to two 16-rank MFMA K-steps per batch of loads
+  constexpr bool T_LDS = NTR > 0 && NTR <= 2;
+  constexpr int TROWB = RP * 4;          // bytes of one t row
+  static_assert(256 * 32 * 4 <= 2 * 16384 && 16384 <= (int)sizeof(I4Slot), "t tile fits slots 6 and 7");
+  // t row r of the block lives at byte r * TROWB of the tile: the first 16 KB in slot 6, the rest
+  // in slot 7
+  auto t_row_ptr = [&](int r) -> const uint8_t* {
+    const int byte = r * TROWB;
+    return byte < 16384 ? reinterpret_cast<const uint8_t*>(ring[6]) + byte
+                        : reinterpret_cast<const uint8_t*>(ring[7]) + (byte - 16384);
+  };
+  v4i LB[KS][2];
+  float4 tv[KS][I4_MT][2];
+  auto lr_load = [&](int k0) {  // L2 operands, and t when it is not staged in LDS
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int kk = k0 + 16 * s;
+      if (kk >= RP) break;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        LB[s][j] = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 64 + j * 32 + lr) * RP + kk + 8 * lh);
+      if (!T_LDS) {
+#pragma unroll
+        for (int i = 0; i < I4_MT; ++i) {
+          const float* tp = xl1 + (size_t)(m0 + wm * 128 + i * 32 + lr) * RP + kk + 8 * lh;
+          tv[s][i][0] = *reinterpret_cast<const float4*>(tp);
+          tv[s][i][1] = *reinterpret_cast<const float4*>(tp + 4);
+        }
+      }
+    }
+  };
+  // t from its LDS tile: one asm block with every read and its own wait (the compiler's LDS-DMA
+  // tracking cannot tell slots 6/7 from the ring groups still in flight and would wait for all of
+  // them). Lane address of tile row i: the row's byte in the tile plus 32 lh (ranks 8 lh ..).
+  auto t_from_lds = [&]() {
+    typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
+    uint32_t ad[I4_MT];
+#pragma unroll
+    for (int i = 0; i < I4_MT; ++i)
+      ad[i] = (uint32_t)(uintptr_t)(lds_cptr)t_row_ptr(wm * 128 + i * 32 + lr) + 32 * lh;
+    if constexpr (NTR == 2) {
+      asm volatile(
+          "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:16\n\t"
+          "ds_read_b128 %2, %16 offset:64\n\tds_read_b128 %3, %16 offset:80\n\t"
+          "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:16\n\t"
+          "ds_read_b128 %6, %17 offset:64\n\tds_read_b128 %7, %17 offset:80\n\t"
+          "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:16\n\t"
+          "ds_read_b128 %10, %18 offset:64\n\tds_read_b128 %11, %18 offset:80\n\t"
+          "ds_read_b128 %12, %19\n\tds_read_b128 %13, %19 offset:16\n\t"
+          "ds_read_b128 %14, %19 offset:64\n\tds_read_b128 %15, %19 offset:80\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(tv[0][0][0]), "=&v"(tv[0][0][1]), "=&v"(tv[1][0][0]), "=&v"(tv[1][0][1]),
+            "=&v"(tv[0][1][0]), "=&v"(tv[0][1][1]), "=&v"(tv[1][1][0]), "=&v"(tv[1][1][1]),
+            "=&v"(tv[0][2][0]), "=&v"(tv[0][2][1]), "=&v"(tv[1][2][0]), "=&v"(tv[1][2][1]),
+            "=&v"(tv[0][3][0]), "=&v"(tv[0][3][1]), "=&v"(tv[1][3][0]), "=&v"(tv[1][3][1])
+          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+          : "memory");
+    } else if constexpr (NTR == 1) {
+      asm volatile(
+          "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\t"
+          "ds_read_b128 %2, %9\n\tds_read_b128 %3, %9 offset:16\n\t"
+          "ds_read_b128 %4, %10\n\tds_read_b128 %5, %10 offset:16\n\t"
+          "ds_read_b128 %6, %11\n\tds_read_b128 %7, %11 offset:16\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(tv[0][0][0]), "=&v"(tv[0][0][1]), "=&v"(tv[0][1][0]), "=&v"(tv[0][1][1]),
+            "=&v"(tv[0][2][0]), "=&v"(tv[0][2][1]), "=&v"(tv[0][3][0]), "=&v"(tv[0][3][1])
+          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+          : "memory");
+    }
+  };
+  auto lr_mfma = [&](int k0) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int kk = k0 + 16 * s;
+      if (kk >= RP) break;
+#pragma unroll
+      for (int i = 0; i < I4_MT; ++i) {
+        const float4 t0 = tv[s][i][0], t1 = tv[s][i][1];
+        const v4i TA = v4i{(int)pack_bf16x2(t0.x, t0.y), (int)pack_bf16x2(t0.z, t0.w), (int)pack_bf16x2(t1.x, t1.y),
+                           (int)pack_bf16x2(t1.z, t1.w)};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(TA), as_bf16x8(LB[s][j]), acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  if (NTR > 0) lr_load(0);
+  if (T_LDS) {  // t tile -> slots 6 and 7: TBYTES / 8 bytes per wave, 1 KB per DMA instruction
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+    const __amdgpu_buffer_rsrc_t t_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(xl1 + (size_t)m0 * RP), 0, (m_pad - m0) * TROWB, RSRC_W3);
+    constexpr int TCHUNK = 256 * TROWB / 8;
+#pragma unroll
+    for (int q = 0; q < TCHUNK / 1024; ++q) {
+      const int off = wave * TCHUNK + q * 1024;  // chunks never straddle the 16 KB split
+      uint8_t* dst = off < 16384 ? reinterpret_cast<uint8_t*>(ring[6]) + off
+                                 : reinterpret_cast<uint8_t*>(ring[7]) + (off - 16384);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr_t)dst, 16, 16 * lane, off, 0, 0);
+    }
+  }
+
   // prologue: zero words of every slot; groups 0 .. NS-3 in flight; group 0 visible
   if (tid < 32) {
 #pragma unroll
@@ -404,6 +511,15 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   for (int s = 0; s < I4_NS - 2; ++s) dma(s, ring[s]);
   wait_vmcnt<3 * (I4_NS - 3)>();
   __builtin_amdgcn_s_barrier();
+  if (NTR > 0) {
+    if (T_LDS) t_from_lds();
+    lr_mfma(0);
+#pragma unroll
+    for (int k0 = 32; k0 < RP; k0 += 32) {
+      lr_load(k0);
+      lr_mfma(k0);
+    }
+  }
   auto a_raw = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i); };
   auto b_raw = [&](const I4Slot* sl, int j) { return *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j); };
   if constexpr (INT4) {
@@ -556,30 +672,6 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     }
   }
   wait_vmcnt<0>();  // no LDS DMA may outlive the block
-
-  // low-rank up projection: acc += bf16(t) · L2 over k = rank index (32x32x16 bf16 MFMA)
-  if (NTR > 0) {
-    constexpr int RP = NTR * 16;
-#pragma unroll
-    for (int kk = 0; kk < RP; kk += 16) {
-      v4i LB[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        LB[j] = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 64 + j * 32 + lr) * RP + kk + 8 * lh);
-#pragma unroll
-      for (int i = 0; i < I4_MT; ++i) {
-        const int trow = m0 + wm * 128 + i * 32 + lr;
-        const float* tp = xl1 + (size_t)trow * RP + kk + 8 * lh;
-        const float4 t0 = *reinterpret_cast<const float4*>(tp);
-        const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
-        const v4i TA = v4i{(int)(bf16_rne(t0.x) | (bf16_rne(t0.y) << 16)), (int)(bf16_rne(t0.z) | (bf16_rne(t0.w) << 16)),
-                           (int)(bf16_rne(t1.x) | (bf16_rne(t1.y) << 16)), (int)(bf16_rne(t1.z) | (bf16_rne(t1.w) << 16))};
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(TA), as_bf16x8(LB[j]), acc[i][j], 0, 0, 0);
-      }
-    }
-  }
 
   // store through LDS, so that every lane writes whole 16-byte row segments: the wave's 128 x 64
   // tile goes out in two halves of 64 rows, staged in the wave's own (now idle) ring slot with a
