@@ -168,6 +168,30 @@ def test_deterministic_and_stream():
         assert np.array_equal(g1[k], g2[k]), k
 
 
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32"])
+@pytest.mark.parametrize("case", [
+    (2000, 512, 8440, 20, True),   # 8 x 33 = 264 tiles (more than the GPU runs at once), 8 groups
+    (2000, 832, 8440, 20, True),   # 13 groups: the last ring round is partial
+    (1999, 512, 8443, 0, False),   # N not a multiple of 8: element stores
+])
+def test_many_tiles_ragged(fmt, case):
+    """More 256 x 256 output tiles than the GPU has compute units, with ragged M and N, so the last
+    tile row and column are partial (Y checked on sampled rows, every column, and the canary
+    columns past N)."""
+    m, k, n, r, with_bias = case
+    d = synth.make_layer(m, k, n, n_outliers=3, outlier_scale=30.0, seed=m + k + n)
+    lam, inv = _smooth(d)
+    ref = oracle_weights(d, r, fmt, lam)
+    bias = (synth.f32_to_bf16_bits(np.random.default_rng(n).standard_normal(n).astype(np.float32))
+            if with_bias else None)
+    print(f"[many tiles] {fmt} M={m} K={k} N={n} r={r} bias={with_bias}", flush=True)
+    g = gpu_layer(d, lam, inv, r, fmt, ref, bias=bias, pad_cols=5)
+    check_activation_side(d, inv, ref, fmt, g)
+    rows = _sample_rows(m, n=40, seed=k)
+    check_y(g, O.linear(d["x"][rows], inv, ref, bias)["y"], rows)
+    assert np.all(g["y"][:, n:] == -7.0), "wrote outside the M x N block"
+
+
 # ------------------------------------------------------------------------------- full sizes
 _CACHE = {}
 

@@ -23,6 +23,8 @@ inline w4a4_status_t check_shape(int M, int N, int K, int rank, int fmt) {
   // sizes must stay addressable with 32-bit element offsets inside the kernels
   if ((long long)rows_pad_of(M) * K > (1LL << 31) || (long long)rows_pad_of(N) * K > (1LL << 31))
     return W4A4_ERR_INVALID_ARG;
+  // t (fp32) and L2^T (bf16) are addressed with 32-bit byte offsets too
+  if ((long long)rows_pad_of(M) * rank_pad_of(rank) * 4 >= (1LL << 31)) return W4A4_ERR_INVALID_ARG;
   return W4A4_OK;
 }
 
