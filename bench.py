@@ -8,7 +8,8 @@ low-rank up projection. Prints ONE JSON line on stdout (diagnostics go to stderr
 
   value      effective TOPS = (2·M·N·K + 2·M·r·(K+N)) / time per step (whole job, one GPU)
   roofline   the GEMM kernel: algorithmic ops per launch / its average launch time (HIP events on
-             the launch stream) against the MI355X dense int8/fp8 MFMA peak (5.0 POP/s) for INT4,
+             the launch stream around each GEMM launch of `steps` further steps, right after the
+             timed region) against the MI355X dense int8/fp8 MFMA peak (5.0 POP/s) for INT4,
              or the MXFP4 peak (10.1 PFLOP/s) for the FP4 variant
   cpu_baseline  the numpy oracle's forward pass on a bounded sample of rows of the same layer
 """
@@ -69,25 +70,33 @@ def cpu_baseline(d, lam, inv, budget_s=20.0):
     t0 = time.perf_counter()
     prep = O.prepare_weights(d["w"], lam, d["rank"], d["fmt"])
     log(f"[cpu] oracle weight prep {time.perf_counter() - t0:.1f}s (not timed)")
-    rows, spent, result = 64, 0.0, None
-    while True:
-        xs = d["x"][:rows]
+    M = d["x"].shape[0]
+    rows, spent = 64, 0.0
+    while True:  # grow the sample (up to all of X) until one forward takes a quarter of the budget
         t0 = time.perf_counter()
-        O.linear(xs, inv, prep)
+        O.linear(d["x"][:rows], inv, prep)
         dt = time.perf_counter() - t0
         spent += dt
-        result = (rows, dt)
-        if dt >= budget_s / 4 or spent >= budget_s or rows * 2 > d["x"].shape[0]:
+        if dt >= budget_s / 4 or spent >= budget_s or rows == M:
             break
-        rows *= 2
-    rows, dt = result
+        rows = min(rows * 2, M)
+    times = [dt]
+    while spent < budget_s / 2:  # repeat the final sample to about half the budget in all
+        t0 = time.perf_counter()
+        O.linear(d["x"][:rows], inv, prep)
+        times.append(time.perf_counter() - t0)
+        spent += times[-1]
+    dt = float(np.mean(times))
     ops = layer_ops(rows, d["N"], d["K"], d["rank"])
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
+    try:  # threads the BLAS behind numpy ran with (the oracle's matmuls), bounded by the CPU set
+        from threadpoolctl import threadpool_info
+        cores = max([p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except ImportError:
+        cores = 1
+    cores = min(cores, len(os.sched_getaffinity(0)))
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} of {d['x'].shape[0]} rows of X ({dt:.2f}s, numpy fp64 forward incl. quantization)"}
+            "sample": f"{rows} of {M} rows of X, {len(times)} run(s) of {dt:.2f}s each (numpy fp64 forward incl. "
+                      f"quantization; {spent:.1f}s of CPU work in all)"}
 
 
 def main():
@@ -131,29 +140,39 @@ def main():
     acts = layer.act_buffers(M)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+    def step():
         layer.quantize(x)
-        if ev:
-            ev[1].record(stream)
         layer.gemm(acts, M, y)
-        if ev:
-            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed region: exactly `steps` steps, nothing else on the stream
+    e_begin, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e_begin.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step()
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    g_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    ev_ms_step = e_begin.elapsed_time(e_end) / args.steps
+
+    # per-kernel launch durations: the same steps again, with HIP events on the launch stream
+    # between the kernels (outside the timed region: the events themselves cost a little time)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        layer.quantize(x)
+        evs[i][1].record(stream)
+        layer.gemm(acts, M, y)
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    q_avg = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    g_avg = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
     # cold-cache view: overwrite a 1 GiB buffer (> 256 MB MALL + L2) before each step, kernels timed by events
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -161,7 +180,11 @@ def main():
     for i in range(min(args.steps, 20)):
         flush.fill_(float(i))
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        step(ev)
+        ev[0].record(stream)
+        layer.quantize(x)
+        ev[1].record(stream)
+        layer.gemm(acts, M, y)
+        ev[2].record(stream)
         torch.cuda.synchronize()
         cq.append(ev[0].elapsed_time(ev[1]))
         cg.append(ev[1].elapsed_time(ev[2]))
@@ -170,7 +193,6 @@ def main():
     ops = layer_ops(M, N, K, r)
     ms_step = wall * 1e3 / args.steps
     value = ops / (ms_step * 1e-3) / 1e12
-    g_avg = float(g_ms.mean())
     achieved = ops / (g_avg * 1e-3) / 1e12
     peak = PEAK_TOPS[fmt]
     qbytes = quantize_bytes(M, K, r, fmt)
@@ -179,16 +201,16 @@ def main():
     out = {
         "metric": "effective TOPS of fused W4A4+rank-32 linear at FLUX shapes; % MFMA peak",
         "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(ms_step, 5), "event_ms_per_step": round(ev_ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int4" if fmt == "int4_g64" else "fp4", "data": "synthetic (seeded FLUX-shaped layer; random weights)",
         "config": {"workload": args.workload, "M": M, "K": K, "N": N, "rank": r, "format": fmt,
                    "ops_per_step": ops, "peak_frac_of_step": round(value / peak, 4)},
-        "roofline": {"bound": "mfma", "kernel": f"gemm_{'int4' if fmt == 'int4_g64' else 'mxfp4'}_kernel",
+        "roofline": {"bound": "mfma", "kernel": f"gemm_kernel<{0 if fmt == 'int4_g64' else 1},{prep['rank_pad'] // 16}>",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "avg_launch_ms": round(g_avg, 5), "algorithmic_ops_per_launch": ops},
         "kernels": {
-            "quantize_act": {"avg_ms_warm": round(float(q_ms.mean()), 5), "avg_ms_cold": round(float(np.mean(cq)), 5),
+            "quantize_act": {"avg_ms_warm": round(q_avg, 5), "avg_ms_cold": round(float(np.mean(cq)), 5),
                              "algorithmic_bytes": qbytes,
                              "GB/s_cold": round(qbytes / (np.mean(cq) * 1e-3) / 1e9, 1),
                              "hbm_frac_cold": round(qbytes / (np.mean(cq) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
