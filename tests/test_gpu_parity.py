@@ -258,6 +258,26 @@ def test_full_size_lora_merge():
     assert np.abs(yz - want).max() <= TOL * np.abs(want).max()
 
 
+def test_unfused_lowrank_ablation():
+    """The bench's unfused baseline (rank-0 main branch of this library on the residual codes, the
+    low-rank branch as separate library GEMMs) computes the same layer: Y within the same bound."""
+    import bench
+    d = synth.make_layer(300, 512, 640, n_outliers=5, outlier_scale=30.0, seed=11)
+    lam, inv = _smooth(d)
+    ref = oracle_weights(d, 32, "int4_g64", lam)
+    l1b, l2b = O.f32_to_bf16_bits(ref["l1"]), O.f32_to_bf16_bits(ref["l2"])
+    prep = w4.prepare_weights(d["w"], lam, 32, "int4_g64", l1b, l2b)
+    dev = torch.device("cuda")
+    layer_u = bench.unfused_layer(prep, inv, dev)
+    l1s, l2 = bench.unfused_lowrank_factors(prep, inv, dev)
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((300, 640), dtype=torch.bfloat16, device=dev)
+    bench.unfused_step(layer_u, layer_u.act_buffers(300), x, y, l1s, l2)
+    torch.cuda.synchronize()
+    check_y(dict(y=O.bf16_bits_to_f32(y.view(torch.int16).cpu().numpy().view(np.uint16))),
+            O.linear(d["x"], inv, ref)["y"])
+
+
 @pytest.mark.parametrize("m", [1024, 4608, 16384])
 def test_full_size_mxfp4_sweep(m):
     d, lam, inv, ref = _full("mxfp4_sweep")
