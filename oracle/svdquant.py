@@ -333,6 +333,49 @@ def prepare_weights(w_bits: np.ndarray, lam: np.ndarray, rank: int, fmt: str = F
                 cw=cw, sw=sw, fmt=fmt)
 
 
+def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarray:
+    """The 4-bit tensor's values in fp64 (§3: the low-bit tensor times its scale)."""
+    if fmt == FMT_INT4_G64:
+        return dequant_int4_g64(codes, scales)
+    return dequant_mxfp4_b32(codes, scales)
+
+
+def split_error(w_hat: np.ndarray, l1: np.ndarray, l2: np.ndarray, cw: np.ndarray, sw: np.ndarray,
+                fmt: str) -> float:
+    """||Ŵ − (L1 L2)ᵀ − deq(Q(R))||_F in fp64: the part of the smoothed weight that neither the
+    16-bit branch nor the 4-bit branch represents."""
+    miss = np.asarray(w_hat, np.float64) - lowrank_product_t(l1, l2).T - dequantize(cw, sw, fmt)
+    return float(np.sqrt(np.sum(miss * miss)))
+
+
+def prepare_weights_refined(w_bits: np.ndarray, lam: np.ndarray, rank: int, fmt: str = FMT_INT4_G64,
+                            iters: int = 3):
+    """§4.2's iterative refinement of the split. The page says only that iterative updates reduce
+    the quantization error further and that the result with the smallest error after several
+    iterations is kept; the reading taken: alternate the two branches. Iteration 0 is
+    ``prepare_weights``; iteration i >= 1 re-fits the low-rank branch to what the current 4-bit
+    branch misses, L1·L2 = SVD_r(Ŵ − deq(Q(R_{i-1})))ᵀ, and quantizes R_i = Ŵ − (L1·L2)ᵀ afresh.
+    Every iteration is scored by ``split_error``; the one with the smallest error wins (the
+    earliest on ties). Returns ``prepare_weights``' dict plus ``errors`` (all iterations) and
+    ``iteration`` (the winner)."""
+    w_hat = smooth_weights(bf16_bits_to_f32(w_bits), lam)
+    target = w_hat
+    errors, best = [], None
+    for it in range(iters + 1):
+        l1, l2 = lowrank_split(target, rank)
+        r = residual(w_hat, l1, l2)
+        cw, sw = quantize(r, fmt)
+        e = split_error(w_hat, l1, l2, cw, sw, fmt)
+        errors.append(e)
+        if best is None or e < errors[best[0]]:
+            best = (it, dict(w_hat=w_hat, l1=np.asarray(l1, np.float32), l2=np.asarray(l2, np.float32), r=r,
+                             cw=cw, sw=sw, fmt=fmt))
+        target = w_hat - dequantize(cw, sw, fmt)
+    out = best[1]
+    out.update(errors=errors, iteration=best[0])
+    return out
+
+
 def quantize_activations(x_bits: np.ndarray, inv_lam: np.ndarray, l1: np.ndarray, fmt: str = FMT_INT4_G64):
     """The activation side: X̂, its codes and scales, and the down projection t (fp64)."""
     x_hat = smooth_activations(bf16_bits_to_f32(x_bits), inv_lam)

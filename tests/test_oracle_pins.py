@@ -256,6 +256,50 @@ def test_residual_is_narrower_than_smoothed_weight():
     assert np.linalg.norm(prep["r"]) < np.linalg.norm(prep["w_hat"])
 
 
+def test_split_error_closed_form():
+    """What both branches miss: zero when the 4-bit branch represents R exactly (every group is
+    q·2^-3 with a 7 in it, rank 0); exactly |δ| after one element moves by δ less than half a
+    quantization step (the code rounds the move away)."""
+    rng = np.random.default_rng(5)
+    q = rng.integers(-7, 8, size=(8, 128)).astype(np.float64)
+    q[:, 0] = 7
+    q[:, 64] = -7
+    q[3, 5] = 2
+    lam = np.ones(128, np.float32)
+    w = q * 2.0 ** -3
+    prep = O.prepare_weights(O.f32_to_bf16_bits(w.astype(np.float32)), lam, 0)
+    assert O.split_error(prep["w_hat"], prep["l1"], prep["l2"], prep["cw"], prep["sw"], "int4_g64") == 0.0
+    w[3, 5] += 2.0 ** -6
+    prep = O.prepare_weights(O.f32_to_bf16_bits(w.astype(np.float32)), lam, 0)
+    assert O.split_error(prep["w_hat"], prep["l1"], prep["l2"], prep["cw"], prep["sw"], "int4_g64") == 2.0 ** -6
+
+
+def test_refine_iteration0_is_the_plain_split():
+    d = synth.workload("tiny")
+    lam, _ = O.smooth_factors(O.column_absmax(O.bf16_bits_to_f32(d["x"])), O.column_absmax(O.bf16_bits_to_f32(d["w"])))
+    for fmt in ("int4_g64", "mxfp4_b32"):
+        plain = O.prepare_weights(d["w"], lam, 16, fmt)
+        rf = O.prepare_weights_refined(d["w"], lam, 16, fmt, iters=0)
+        for k in ("l1", "l2", "cw", "sw"):
+            assert np.array_equal(rf[k], plain[k]), k
+        assert rf["iteration"] == 0
+        assert rf["errors"] == [O.split_error(plain["w_hat"], plain["l1"], plain["l2"], plain["cw"], plain["sw"], fmt)]
+
+
+def test_refine_keeps_the_smallest_error_and_reduces_it():
+    """§4.2: iterative updates reduce the quantization error, and the result with the smallest
+    error is kept. The kept arrays reproduce the reported error; on the outlier layer the error
+    falls below the plain split's."""
+    d = synth.make_layer(96, 256, 192, n_outliers=4, outlier_scale=30.0, seed=21)
+    lam, _ = O.smooth_factors(O.column_absmax(O.bf16_bits_to_f32(d["x"])), O.column_absmax(O.bf16_bits_to_f32(d["w"])))
+    for fmt in ("int4_g64", "mxfp4_b32"):
+        rf = O.prepare_weights_refined(d["w"], lam, 8, fmt, iters=4)
+        e = O.split_error(rf["w_hat"], rf["l1"], rf["l2"], rf["cw"], rf["sw"], fmt)
+        assert e == rf["errors"][rf["iteration"]] == min(rf["errors"])
+        assert min(rf["errors"]) < 0.97 * rf["errors"][0]
+        assert rf["errors"].index(min(rf["errors"])) == rf["iteration"]
+
+
 # ---------------------------------------------------------------- special cases of the layer
 def test_rank0_unquantized_is_plain_gemm():
     d = synth.workload("tiny")
