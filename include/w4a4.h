@@ -134,6 +134,25 @@ w4a4_status_t w4a4_prepare_weights(const uint16_t* W, int N, int K, const float*
                                    uint16_t* L1_out, uint16_t* L2_out);
 
 /*
+ * Iterative refinement of the split (§4.2: iterative updates lower the quantization error and the
+ * result with the smallest error after several iterations is kept). Iteration 0 is the split of
+ * w4a4_prepare_weights (own SVD); iteration i >= 1 re-fits the low-rank branch to what the
+ * current 4-bit branch misses, L1·L2 = rank-r SVD of (Ŵ − deq(Q(R_{i-1})))ᵀ, and quantizes
+ * R_i = Ŵ − (L1·L2)ᵀ afresh. Each iteration is scored by ||Ŵ − (L1·L2)ᵀ − deq(Q(R))||_F (fp64);
+ * the outputs (same buffers and layouts as w4a4_prepare_weights) hold the iteration with the
+ * smallest score, the earliest on ties.
+ *   iters      0 .. 64 further iterations (0 gives w4a4_prepare_weights' result)
+ *   errors     [iters + 1] fp64 host output, the score of every iteration (may be NULL)
+ *   best_iter  host output, the iteration kept (may be NULL)
+ * Host buffers; synchronous; thread-safe; uses several CPU threads. Errors as
+ * w4a4_prepare_weights (W4A4_ERR_INVALID_ARG also for iters outside 0 .. 64).
+ */
+w4a4_status_t w4a4_prepare_weights_refined(const uint16_t* W, int N, int K, const float* lambda, int rank,
+                                           int fmt, int iters, uint8_t* wq, void* wscale, uint16_t* l1t,
+                                           uint16_t* l2t, uint16_t* L1_out, uint16_t* L2_out, double* errors,
+                                           int* best_iter);
+
+/*
  * LoRA merge without re-quantization (§2, §5.2: the low-rank branch absorbs a LoRA by growing
  * its rank): L1' = [L1 | A], L2' = [L2 ; B], rank' = rank + ra. Reads the library-layout
  * factors (l1t [rank_pad][K], l2t [n_pad][rank_pad]) and writes the merged ones

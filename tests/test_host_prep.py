@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "w4a4.h")
 
 def test_library_exports_every_declared_symbol():
     decl = set(re.findall(r"\b(w4a4_[a-z0-9_]+)\s*\(", open(HEADER).read()))
-    assert len(decl) == 11, sorted(decl)
+    assert len(decl) == 12, sorted(decl)
     L = w4.lib()
     missing = [n for n in decl if not hasattr(L, n)]
     assert not missing, missing
@@ -194,6 +194,49 @@ def test_own_svd_deterministic():
     a = w4.prepare_weights(d["w"], lam, 16)
     b = w4.prepare_weights(d["w"], lam, 16)
     assert all(np.array_equal(a[k], b[k]) for k in ("wq", "wscale", "l1t", "l2t"))
+
+
+def _split_error_of(prep, w_bits, lam, fmt):
+    """The oracle's split error of a library preparation (codes and scales decoded canonically)."""
+    n, k = w_bits.shape
+    canon = w4.codes_to_canonical(prep["wq"], n, k, fmt)
+    lo, hi = canon & 0xF, canon >> 4
+    nib = np.empty((n, k), np.uint8)
+    nib[:, 0::2], nib[:, 1::2] = lo, hi
+    sc = w4.scales_to_canonical(prep["wscale"], n, k, fmt)
+    if fmt == "int4_g64":
+        codes = np.where(nib >= 8, nib.astype(np.int16) - 16, nib.astype(np.int16))
+        scales = O.bf16_bits_to_f32(sc)
+    else:
+        codes, scales = nib, sc
+    w_hat = O.smooth_weights(O.bf16_bits_to_f32(w_bits), lam)
+    l1 = O.bf16_bits_to_f32(prep["l1"])
+    l2 = O.bf16_bits_to_f32(prep["l2"])
+    return O.split_error(w_hat, l1, l2, codes, scales, fmt)
+
+
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32"])
+def test_refined_split(fmt):
+    """Iterative refinement (§4.2): iteration 0 is the plain preparation byte for byte; the kept
+    iteration's arrays reproduce its reported score (recomputed by the oracle) and have the
+    smallest score; the refinement lowers the error, as the oracle's own refinement does."""
+    d = synth.make_layer(96, 256, 192, n_outliers=4, outlier_scale=30.0, seed=21)
+    lam, _ = O.smooth_factors(O.column_absmax(O.bf16_bits_to_f32(d["x"])), O.column_absmax(O.bf16_bits_to_f32(d["w"])))
+    plain = w4.prepare_weights(d["w"], lam, 8, fmt)
+    r0 = w4._prepare_weights_refined(d["w"], lam, 8, fmt, 0)
+    for key in ("wq", "wscale", "l1t", "l2t", "l1", "l2"):
+        assert np.array_equal(r0[key], plain[key]), key
+    assert r0["errors"][0] == pytest.approx(_split_error_of(plain, d["w"], lam, fmt), rel=1e-12)
+    rf = w4.prepare_weights(d["w"], lam, 8, fmt, refine_iters=4)
+    e = rf["errors"]
+    assert len(e) == 5 and e[rf["iteration"]] == min(e) and e.index(min(e)) == rf["iteration"]
+    assert _split_error_of(rf, d["w"], lam, fmt) == pytest.approx(e[rf["iteration"]], rel=1e-12)
+    assert min(e) < 0.97 * e[0]
+    ref = O.prepare_weights_refined(d["w"], lam, 8, fmt, iters=4)
+    assert e[0] == pytest.approx(ref["errors"][0], rel=2e-3)          # own SVD vs LAPACK
+    assert min(e) == pytest.approx(min(ref["errors"]), rel=2e-2)
+    with pytest.raises(w4.W4A4Error):
+        w4._prepare_weights_refined(d["w"], lam, 8, fmt, 65)
 
 
 def test_append_lowrank():

@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "w4a4_column_absmax": [P, I, I, I, P],
             "w4a4_smooth_factors": [P, P, I, F, P, P],
             "w4a4_prepare_weights": [P, I, I, P, I, I, P, P, P, P, P, P, P, P],
+            "w4a4_prepare_weights_refined": [P, I, I, P, I, I, I, P, P, P, P, P, P, P, P],
             "w4a4_append_lowrank": [P, P, I, I, I, P, P, I, P, P],
             "w4a4_codes_to_canonical": [P, I, I, I, P],
             "w4a4_scales_to_canonical": [P, I, I, I, P],
@@ -128,8 +129,13 @@ def smooth_factors(amax_x: np.ndarray, amax_w: np.ndarray, alpha: float = 0.5):
     return lam, inv
 
 
-def prepare_weights(w_bits: np.ndarray, lam: np.ndarray, rank: int, fmt=FMT_INT4_G64, l1_bits=None, l2_bits=None):
-    """Host weight preparation. Returns numpy arrays in library layout plus the bf16 factors used."""
+def prepare_weights(w_bits: np.ndarray, lam: np.ndarray, rank: int, fmt=FMT_INT4_G64, l1_bits=None, l2_bits=None,
+                    refine_iters: int = 0):
+    """Host weight preparation. Returns numpy arrays in library layout plus the bf16 factors used.
+    With ``refine_iters`` > 0 the split is refined iteratively (w4a4_prepare_weights_refined) and the
+    result also holds the score of every iteration (``errors``) and the one kept (``iteration``)."""
+    if refine_iters:
+        return _prepare_weights_refined(w_bits, lam, rank, fmt, refine_iters)
     w = _c(w_bits, np.uint16)
     n, k = w.shape
     f = _fmt(fmt)
@@ -148,6 +154,28 @@ def prepare_weights(w_bits: np.ndarray, lam: np.ndarray, rank: int, fmt=FMT_INT4
         _hptr(l1t), _hptr(l2t), _hptr(l1o), _hptr(l2o)))
     return dict(wq=wq, wscale=ws, l1t=l1t[: sz["l1t"] // 2], l2t=l2t[: sz["l2t"] // 2], l1=l1o, l2=l2o,
                 N=n, K=k, rank=rank, fmt=f, n_pad=sz["n_pad"], rank_pad=sz["rank_pad"])
+
+
+def _prepare_weights_refined(w_bits, lam, rank, fmt, iters):
+    w = _c(w_bits, np.uint16)
+    n, k = w.shape
+    f = _fmt(fmt)
+    sz = buffer_sizes(1, n, k, rank, f)
+    lam = _c(lam, np.float32)
+    wq = np.empty(sz["wq"], np.uint8)
+    ws = np.empty(sz["wscale"], np.uint8)
+    l1t = np.empty(max(sz["l1t"] // 2, 1), np.uint16)
+    l2t = np.empty(max(sz["l2t"] // 2, 1), np.uint16)
+    l1o = np.empty((k, rank), np.uint16)
+    l2o = np.empty((rank, n), np.uint16)
+    errs = np.empty(iters + 1, np.float64)
+    best = ctypes.c_int(-1)
+    _check("w4a4_prepare_weights_refined", lib().w4a4_prepare_weights_refined(
+        _hptr(w), n, k, _hptr(lam), rank, f, int(iters), _hptr(wq), _hptr(ws), _hptr(l1t), _hptr(l2t),
+        _hptr(l1o), _hptr(l2o), _hptr(errs), ctypes.addressof(best)))
+    return dict(wq=wq, wscale=ws, l1t=l1t[: sz["l1t"] // 2], l2t=l2t[: sz["l2t"] // 2], l1=l1o, l2=l2o,
+                N=n, K=k, rank=rank, fmt=f, n_pad=sz["n_pad"], rank_pad=sz["rank_pad"], errors=errs.tolist(),
+                iteration=best.value)
 
 
 def append_lowrank(l1t: np.ndarray, l2t: np.ndarray, K: int, N: int, rank: int, a_bits: np.ndarray, b_bits: np.ndarray):

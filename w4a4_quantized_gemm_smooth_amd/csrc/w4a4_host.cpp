@@ -343,6 +343,132 @@ bool truncated_svd(const double* W, int N, int K, int r, std::vector<double>& u,
 
 }  // namespace
 
+namespace {
+
+// E2M1 code -> value: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 is the sign.
+double e2m1_value(uint8_t c) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  return (c & 8) ? -mag[c & 7] : mag[c & 7];
+}
+
+// One split of the smoothed weight (§4.2): factors from the rank-r SVD of `target` (or the given
+// bf16 factors), the residual R = Ŵ − (L1·L2)ᵀ from the bf16 factors, its 4-bit codes and scales
+// in library layout. With `deq` it also returns deq(Q(R)) [N][K], and with `err` the split error
+// ||Ŵ − (L1·L2)ᵀ − deq(Q(R))||_F (fp64, summed per row in order, rows in order).
+bool split_once(const std::vector<double>& what, const double* target, int N, int K, int rank, int fmt,
+                const uint16_t* L1_in, const uint16_t* L2_in, uint8_t* wq, void* wscale, std::vector<uint16_t>& L1,
+                std::vector<uint16_t>& L2, std::vector<double>* deq, double* err) {
+  const int np = rows_pad_of(N), G = K / W4A4_GROUP;
+  L1.assign(size_t(K) * rank, 0);
+  L2.assign(size_t(rank) * N, 0);
+  if (rank > 0) {
+    if (L1_in) {
+      std::memcpy(L1.data(), L1_in, L1.size() * 2);
+      std::memcpy(L2.data(), L2_in, L2.size() * 2);
+    } else {
+      std::vector<double> u, sig, v;
+      if (!truncated_svd(target, N, K, rank, u, sig, v)) return false;
+      for (int k = 0; k < K; ++k)
+        for (int i = 0; i < rank; ++i) L1[size_t(k) * rank + i] = f32_to_bf16(float(u[size_t(i) * K + k] * sig[i]));
+      for (int i = 0; i < rank; ++i)
+        for (int n = 0; n < N; ++n) L2[size_t(i) * N + n] = f32_to_bf16(float(v[size_t(i) * N + n]));
+    }
+  }
+  std::vector<double> l1d(L1.size()), l2d(L2.size());
+  for (size_t i = 0; i < L1.size(); ++i) l1d[i] = bf16_to_f32(L1[i]);
+  for (size_t i = 0; i < L2.size(); ++i) l2d[i] = bf16_to_f32(L2[i]);
+  // residual and its quantization, one weight row per task
+  const bool mx = fmt == W4A4_FMT_MXFP4_B32;
+  std::memset(wq, 0, size_t(np) * K / 2);
+  std::memset(wscale, 0, mx ? size_t(K / W4A4_MX_BLOCK) * np : size_t(G) * np * 2);
+  if (deq) deq->assign(size_t(N) * K, 0.0);
+  std::vector<double> row_err(static_cast<size_t>(N), 0.0);
+  parallel_for(N, [&](int b, int e, int) {
+    std::vector<float> rrow(static_cast<size_t>(K));
+    std::vector<double> lrow(static_cast<size_t>(K));
+    for (int n = b; n < e; ++n) {
+      for (int k = 0; k < K; ++k) {
+        double d = 0.0;
+        for (int i = 0; i < rank; ++i) d += l1d[size_t(k) * rank + i] * l2d[size_t(i) * N + n];
+        lrow[k] = d;
+        rrow[k] = float(what[size_t(n) * K + k] - d);
+      }
+      double acc = 0.0;
+      for (int g = 0; g < G; ++g) {
+        uint8_t* dst = wq + (size_t(g) * np + n) * 32;
+        double v[W4A4_GROUP];
+        if (mx) {
+          uint8_t* s8 = static_cast<uint8_t*>(wscale);
+          uint8_t* e_lo = &s8[size_t(2 * g) * np + n];
+          uint8_t* e_hi = &s8[size_t(2 * g + 1) * np + n];
+          quant_mxfp4_chunk(rrow.data() + size_t(g) * W4A4_GROUP, dst, e_lo, e_hi);
+          for (int k = 0; k < W4A4_GROUP; ++k) {
+            const uint8_t c = uint8_t((dst[k / 2] >> (4 * (k & 1))) & 15u);
+            v[k] = std::ldexp(e2m1_value(c), int(k < W4A4_MX_BLOCK ? *e_lo : *e_hi) - 127);
+          }
+        } else {
+          uint16_t* sb = &static_cast<uint16_t*>(wscale)[size_t(g) * np + n];
+          quant_int4_group(rrow.data() + size_t(g) * W4A4_GROUP, dst, sb);
+          int q[W4A4_GROUP];
+          unfold_int4_group(dst, q);
+          const double sc = bf16_to_f32(*sb);
+          for (int k = 0; k < W4A4_GROUP; ++k) v[k] = double(q[k]) * sc;
+        }
+        for (int k = 0; k < W4A4_GROUP; ++k) {
+          const size_t idx = size_t(n) * K + size_t(g) * W4A4_GROUP + k;
+          if (deq) (*deq)[idx] = v[k];
+          const double miss = what[idx] - lrow[size_t(g) * W4A4_GROUP + k] - v[k];
+          acc += miss * miss;
+        }
+      }
+      row_err[n] = acc;
+    }
+  });
+  if (err) {
+    double tot = 0.0;
+    for (int n = 0; n < N; ++n) tot += row_err[n];
+    *err = std::sqrt(tot);
+  }
+  return true;
+}
+
+// Ŵ = W · diag(λ) in fp64 (exact: bf16 x fp32 fits in 53 bits)
+std::vector<double> smoothed_weight(const uint16_t* W, int N, int K, const float* lambda) {
+  std::vector<double> what(size_t(N) * K);
+  parallel_for(N, [&](int b, int e, int) {
+    for (int n = b; n < e; ++n)
+      for (int k = 0; k < K; ++k)
+        what[size_t(n) * K + k] = double(bf16_to_f32(W[size_t(n) * K + k])) * double(lambda[k]);
+  });
+  return what;
+}
+
+void write_factors(const std::vector<uint16_t>& L1, const std::vector<uint16_t>& L2, int N, int K, int rank,
+                   uint16_t* l1t, uint16_t* l2t, uint16_t* L1_out, uint16_t* L2_out) {
+  const int np = rows_pad_of(N), rp = rank_pad_of(rank);
+  std::memset(l1t, 0, size_t(rp) * K * 2);
+  std::memset(l2t, 0, size_t(np) * rp * 2);
+  for (int k = 0; k < K; ++k)
+    for (int i = 0; i < rank; ++i) l1t[size_t(i) * K + k] = L1[size_t(k) * rank + i];
+  for (int i = 0; i < rank; ++i)
+    for (int n = 0; n < N; ++n) l2t[size_t(n) * rp + i] = L2[size_t(i) * N + n];
+  if (L1_out) std::memcpy(L1_out, L1.data(), L1.size() * 2);
+  if (L2_out) std::memcpy(L2_out, L2.data(), L2.size() * 2);
+}
+
+w4a4_status_t check_prepare_args(const uint16_t* W, int N, int K, const float* lambda, int rank, int fmt,
+                                 uint8_t* wq, void* wscale, uint16_t* l1t, uint16_t* l2t) {
+  w4a4_status_t st = check_shape(1, N, K, rank, fmt);
+  if (st != W4A4_OK) return st;
+  if (!W || !lambda || !wq || !wscale) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!l1t || !l2t)) return W4A4_ERR_INVALID_ARG;
+  for (int k = 0; k < K; ++k)
+    if (!std::isfinite(lambda[k]) || !(lambda[k] > 0.0f)) return W4A4_ERR_INVALID_ARG;
+  return W4A4_OK;
+}
+
+}  // namespace
+
 // ================================================================================ C ABI (host)
 extern "C" {
 
@@ -414,80 +540,61 @@ w4a4_status_t w4a4_smooth_factors(const float* amax_x, const float* amax_w, int 
   return W4A4_OK;
 }
 
+
 w4a4_status_t w4a4_prepare_weights(const uint16_t* W, int N, int K, const float* lambda, int rank,
                                    int fmt, const uint16_t* L1_in, const uint16_t* L2_in,
                                    uint8_t* wq, void* wscale, uint16_t* l1t, uint16_t* l2t,
                                    uint16_t* L1_out, uint16_t* L2_out) {
-  w4a4_status_t st = check_shape(1, N, K, rank, fmt);
+  w4a4_status_t st = check_prepare_args(W, N, K, lambda, rank, fmt, wq, wscale, l1t, l2t);
   if (st != W4A4_OK) return st;
-  if (!W || !lambda || !wq || !wscale) return W4A4_ERR_INVALID_ARG;
   if ((L1_in == nullptr) != (L2_in == nullptr)) return W4A4_ERR_INVALID_ARG;
-  if (rank > 0 && (!l1t || !l2t)) return W4A4_ERR_INVALID_ARG;
-  for (int k = 0; k < K; ++k)
-    if (!std::isfinite(lambda[k]) || !(lambda[k] > 0.0f)) return W4A4_ERR_INVALID_ARG;
   try {
-    const int np = rows_pad_of(N), rp = rank_pad_of(rank), G = K / W4A4_GROUP;
-    // Ŵ = W · diag(λ) in fp64 (exact: bf16 x fp32 fits in 53 bits)
-    std::vector<double> what(size_t(N) * K);
-    parallel_for(N, [&](int b, int e, int) {
-      for (int n = b; n < e; ++n)
-        for (int k = 0; k < K; ++k)
-          what[size_t(n) * K + k] = double(bf16_to_f32(W[size_t(n) * K + k])) * double(lambda[k]);
-    });
-    // rank-r factors as bf16 values: L1 [K][r], L2 [r][N]
-    std::vector<uint16_t> L1(size_t(K) * rank), L2(size_t(rank) * N);
-    if (rank > 0) {
-      if (L1_in) {
-        std::memcpy(L1.data(), L1_in, L1.size() * 2);
-        std::memcpy(L2.data(), L2_in, L2.size() * 2);
-      } else {
-        std::vector<double> u, sig, v;
-        if (!truncated_svd(what.data(), N, K, rank, u, sig, v)) return W4A4_ERR_NUMERIC;
-        for (int k = 0; k < K; ++k)
-          for (int i = 0; i < rank; ++i)
-            L1[size_t(k) * rank + i] = f32_to_bf16(float(u[size_t(i) * K + k] * sig[i]));
-        for (int i = 0; i < rank; ++i)
-          for (int n = 0; n < N; ++n) L2[size_t(i) * N + n] = f32_to_bf16(float(v[size_t(i) * N + n]));
-      }
-    }
-    std::vector<double> l1d(L1.size()), l2d(L2.size());
-    for (size_t i = 0; i < L1.size(); ++i) l1d[i] = bf16_to_f32(L1[i]);
-    for (size_t i = 0; i < L2.size(); ++i) l2d[i] = bf16_to_f32(L2[i]);
-    // residual and its quantization, one weight row per task
+    const std::vector<double> what = smoothed_weight(W, N, K, lambda);
+    std::vector<uint16_t> L1, L2;
+    if (!split_once(what, what.data(), N, K, rank, fmt, L1_in, L2_in, wq, wscale, L1, L2, nullptr, nullptr))
+      return W4A4_ERR_NUMERIC;
+    if (rank > 0) write_factors(L1, L2, N, K, rank, l1t, l2t, L1_out, L2_out);
+  } catch (const std::bad_alloc&) {
+    return W4A4_ERR_INVALID_ARG;
+  } catch (...) {
+    return W4A4_ERR_NUMERIC;
+  }
+  return W4A4_OK;
+}
+
+w4a4_status_t w4a4_prepare_weights_refined(const uint16_t* W, int N, int K, const float* lambda, int rank,
+                                           int fmt, int iters, uint8_t* wq, void* wscale, uint16_t* l1t,
+                                           uint16_t* l2t, uint16_t* L1_out, uint16_t* L2_out, double* errors,
+                                           int* best_iter) {
+  w4a4_status_t st = check_prepare_args(W, N, K, lambda, rank, fmt, wq, wscale, l1t, l2t);
+  if (st != W4A4_OK) return st;
+  if (iters < 0 || iters > 64) return W4A4_ERR_INVALID_ARG;
+  try {
+    const int np = rows_pad_of(N), G = K / W4A4_GROUP;
     const bool mx = fmt == W4A4_FMT_MXFP4_B32;
-    std::memset(wq, 0, size_t(np) * K / 2);
-    std::memset(wscale, 0, mx ? size_t(K / W4A4_MX_BLOCK) * np : size_t(G) * np * 2);
-    parallel_for(N, [&](int b, int e, int) {
-      std::vector<float> rrow(static_cast<size_t>(K));
-      for (int n = b; n < e; ++n) {
-        for (int k = 0; k < K; ++k) {
-          double d = 0.0;
-          for (int i = 0; i < rank; ++i) d += l1d[size_t(k) * rank + i] * l2d[size_t(i) * N + n];
-          rrow[k] = float(what[size_t(n) * K + k] - d);
-        }
-        for (int g = 0; g < G; ++g) {
-          uint8_t* dst = wq + (size_t(g) * np + n) * 32;
-          if (mx) {
-            uint8_t* s8 = static_cast<uint8_t*>(wscale);
-            quant_mxfp4_chunk(rrow.data() + size_t(g) * W4A4_GROUP, dst, &s8[size_t(2 * g) * np + n],
-                              &s8[size_t(2 * g + 1) * np + n]);
-          } else {
-            quant_int4_group(rrow.data() + size_t(g) * W4A4_GROUP, dst,
-                             &static_cast<uint16_t*>(wscale)[size_t(g) * np + n]);
-          }
-        }
+    const size_t q_bytes = size_t(np) * K / 2, s_bytes = mx ? size_t(K / W4A4_MX_BLOCK) * np : size_t(G) * np * 2;
+    const std::vector<double> what = smoothed_weight(W, N, K, lambda);
+    std::vector<double> target = what, deq;
+    std::vector<uint8_t> q(q_bytes), sc(s_bytes);
+    std::vector<uint16_t> L1, L2;
+    double best = 0.0;
+    int best_it = -1;
+    for (int it = 0; it <= iters; ++it) {
+      double e = 0.0;
+      if (!split_once(what, target.data(), N, K, rank, fmt, nullptr, nullptr, q.data(), sc.data(), L1, L2, &deq, &e))
+        return W4A4_ERR_NUMERIC;
+      if (errors) errors[it] = e;
+      if (best_it < 0 || e < best) {  // the earliest of equal errors stays
+        best = e;
+        best_it = it;
+        std::memcpy(wq, q.data(), q_bytes);
+        std::memcpy(wscale, sc.data(), s_bytes);
+        if (rank > 0) write_factors(L1, L2, N, K, rank, l1t, l2t, L1_out, L2_out);
       }
-    });
-    if (rank > 0) {
-      std::memset(l1t, 0, size_t(rp) * K * 2);
-      std::memset(l2t, 0, size_t(np) * rp * 2);
-      for (int k = 0; k < K; ++k)
-        for (int i = 0; i < rank; ++i) l1t[size_t(i) * K + k] = L1[size_t(k) * rank + i];
-      for (int i = 0; i < rank; ++i)
-        for (int n = 0; n < N; ++n) l2t[size_t(n) * rp + i] = L2[size_t(i) * N + n];
-      if (L1_out) std::memcpy(L1_out, L1.data(), L1.size() * 2);
-      if (L2_out) std::memcpy(L2_out, L2.data(), L2.size() * 2);
+      // the next low-rank branch fits what this 4-bit branch misses
+      for (size_t i = 0; i < target.size(); ++i) target[i] = what[i] - deq[i];
     }
+    if (best_iter) *best_iter = best_it;
   } catch (const std::bad_alloc&) {
     return W4A4_ERR_INVALID_ARG;
   } catch (...) {
