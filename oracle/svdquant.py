@@ -56,8 +56,11 @@ MX_BLOCK = 32         # FP4 variant: block of 32 elements share one power-of-two
 QMAX_FP4 = 6.0        # §3: FP4 with 2 exponent bits and 1 mantissa bit has qmax 6
 E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # magnitude of code 0..7
 
+QMAX_INT8 = 127       # §3 with k = 8 (the 8-bit SVDQuant setting, App. D)
+
 FMT_INT4_G64 = "int4_g64"
 FMT_MXFP4_B32 = "mxfp4_b32"
+FMT_W8A8 = "w8a8"     # per-token INT8 activations, per-output-channel INT8 weights, fp32 scales
 
 
 # ----------------------------------------------------------------------------------------
@@ -303,18 +306,50 @@ def main_branch_mxfp4(cx, ex, cw, ew) -> np.ndarray:
     return y
 
 
+def quant_int8_rows(v: np.ndarray):
+    """The 8-bit setting (App. D): one symmetric INT8 scale per row — per token for activations,
+    per output channel for weights — kept in fp32.
+
+    s = fp32(max|v| / 127); q = clamp(rint(fp32(v · fp32(1/s))), -127, 127); a row whose scale is
+    zero or below 2^-126 gets scale 0 and codes 0. Returns (codes int8 [rows, K], scales float32
+    [rows])."""
+    v = np.asarray(v, dtype=np.float32)
+    amax = np.max(np.abs(v), axis=1)
+    s = (amax / np.float32(QMAX_INT8)).astype(np.float32)
+    s[s < np.float32(2.0 ** -126)] = 0.0
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    inv = np.where(s > 0, np.float32(1.0) / safe, np.float32(0.0)).astype(np.float32)
+    y = (v * inv[:, None]).astype(np.float32)
+    q = np.clip(np.rint(y), -QMAX_INT8, QMAX_INT8).astype(np.int8)
+    return q, s
+
+
+def dequant_int8_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    return np.asarray(q, dtype=np.float64) * np.asarray(s, dtype=np.float64)[:, None]
+
+
+def main_branch_w8a8(qx, sx, qw, sw) -> np.ndarray:
+    """Y_m = s_x[m]·s_w[n]·Σ_k q_x[m,k]·q_w[n,k], the integer sum exact in int64."""
+    p = np.asarray(qx, dtype=np.int64) @ np.asarray(qw, dtype=np.int64).T
+    return (np.asarray(sx, np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]) * p.astype(np.float64)
+
+
 def quantize(v: np.ndarray, fmt: str):
-    """(codes, scales) of a [rows, K] float32 tensor in the given 4-bit format."""
+    """(codes, scales) of a [rows, K] float32 tensor in the given low-bit format."""
     if fmt == FMT_INT4_G64:
         return quant_int4_g64(v)
     if fmt == FMT_MXFP4_B32:
         return quant_mxfp4_b32(v)
+    if fmt == FMT_W8A8:
+        return quant_int8_rows(v)
     raise ValueError(fmt)
 
 
 def main_branch(cx, sx, cw, sw, fmt: str) -> np.ndarray:
     if fmt == FMT_INT4_G64:
         return main_branch_int4(cx, sx, cw, sw)
+    if fmt == FMT_W8A8:
+        return main_branch_w8a8(cx, sx, cw, sw)
     return main_branch_mxfp4(cx, sx, cw, sw)
 
 
@@ -337,6 +372,8 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarray:
     """The 4-bit tensor's values in fp64 (§3: the low-bit tensor times its scale)."""
     if fmt == FMT_INT4_G64:
         return dequant_int4_g64(codes, scales)
+    if fmt == FMT_W8A8:
+        return dequant_int8_rows(codes, scales)
     return dequant_mxfp4_b32(codes, scales)
 
 

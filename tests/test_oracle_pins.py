@@ -115,6 +115,59 @@ def test_int4_representable_roundtrip():
     assert np.array_equal(q2, q)
 
 
+# ---------------------------------------------------------------- INT8 rows (8-bit setting)
+def test_int8_nearest_code_bruteforce():
+    """Each code is a nearest point of the grid s*{-127..127} (slack for the reciprocal)."""
+    v = (RNG.standard_normal((500, 256)) * 10.0 ** RNG.uniform(-3, 3, size=(500, 1))).astype(np.float32)
+    q, s = O.quant_int8_rows(v)
+    sv = s.astype(np.float64)[:, None]
+    grid = np.arange(-127, 128, dtype=np.float64)
+    best = np.abs(v.astype(np.float64)[:, :, None] - sv[:, :, None] * grid[None, None, :]).min(axis=2)
+    mine = np.abs(v.astype(np.float64) - sv * q.astype(np.float64))
+    assert np.all(mine <= best + sv * 2.0 ** -16)
+    assert np.all(mine <= sv * (0.5 + 2.0 ** -16))
+
+
+def test_int8_scale_ties_and_range():
+    """s = fp32(amax/127) per row; the row maximum maps to +-127; with a power-of-two scale the
+    reciprocal is exact and half-way values go to the even code; a zero row gets 0 and 0."""
+    v = np.array([[127, 0.5, 1.5, 2.5, -2.5, 126.5, -3.5, 0]], np.float64) * 2.0 ** -4
+    q, s = O.quant_int8_rows(v)
+    assert s[0] == 2.0 ** -4
+    assert q[0].tolist() == [127, 0, 2, 2, -2, 126, -4, 0]
+    w = (RNG.standard_normal((300, 96)) * 3).astype(np.float32)
+    w[7] = 0
+    q, s = O.quant_int8_rows(w)
+    amax = torch.from_numpy(np.abs(w).max(axis=1))
+    ref = (amax / torch.tensor(127.0, dtype=torch.float32)).numpy()
+    ref[ref < 2.0 ** -126] = 0
+    assert np.array_equal(s, ref)
+    nz = s > 0
+    assert np.all(np.abs(q[nz]).max(axis=1) == 127) and not q[~nz].any() and q.min() >= -127
+
+
+def test_int8_representable_roundtrip():
+    """v = s*q with a power-of-two s and a +-127 in each row re-quantizes to the same codes."""
+    q = RNG.integers(-127, 128, size=(200, 64))
+    q[:, 3] = 127
+    for e in (-20, -3, 4):
+        v = (q * 2.0 ** e).astype(np.float32)
+        q2, s2 = O.quant_int8_rows(v)
+        assert np.all(s2 == 2.0 ** e) and np.array_equal(q2, q)
+
+
+def test_main_branch_w8a8_two_formulas():
+    """s_x s_w (q_x·q_w) (exact integer dot) equals dequant(X)·dequant(W)ᵀ up to fp64 rounding."""
+    x = (RNG.standard_normal((40, 192)) * 2).astype(np.float32)
+    w = (RNG.standard_normal((24, 192)) * 0.05).astype(np.float32)
+    qx, sx = O.quant_int8_rows(x)
+    qw, sw = O.quant_int8_rows(w)
+    a = O.main_branch_w8a8(qx, sx, qw, sw)
+    b = O.dequant_int8_rows(qx, sx) @ O.dequant_int8_rows(qw, sw).T
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12 * np.abs(b).max())
+    assert np.array_equal(O.main_branch(qx, sx, qw, sw, O.FMT_W8A8), a)
+
+
 def test_pack_int4_layout():
     q = np.array([[1, -1, -8, 7, 7, -8, 0, -3]], dtype=np.int8)
     assert O.pack_int4(q).tolist() == [[0xF1, 0x78, 0x87, 0xD0]]
