@@ -27,7 +27,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TOPS = {"int4_g64": 5000.0, "mxfp4_b32": 10100.0}   # dense MFMA peaks (int8/fp8; fp4)
+PEAK_TOPS = {"int4_g64": 5000.0, "mxfp4_b32": 10100.0, "w8a8": 5000.0}   # dense MFMA peaks (int8/fp8; fp4)
+DTYPE = {"int4_g64": "int4", "mxfp4_b32": "fp4", "w8a8": "int8"}
 HBM_PEAK_GBS = 8000.0
 
 
@@ -40,10 +41,43 @@ def layer_ops(M, N, K, r):
 
 
 def quantize_bytes(M, K, r, fmt):
-    """Algorithmic HBM bytes of one activation-kernel launch: read X (bf16) and 1/λ, read L1,
+    """Algorithmic HBM bytes of the activation side of one step: read X (bf16) and 1/λ, read L1,
     write codes, scales and t."""
+    if fmt == "w8a8":
+        return M * K * 2 + K * 4 + r * K * 2 + M * (K + 4 + r * 4)
     scale_bytes = (K // 64) * 2 if fmt == "int4_g64" else (K // 32)
     return M * K * 2 + K * 4 + r * K * 2 + M * (K // 2 + scale_bytes + r * 4)
+
+
+def gemm_kernel_name(fmt, rank_pad):
+    nt = rank_pad // 16
+    return f"gemm_w8a8_kernel<{nt}>" if fmt == "w8a8" else f"gemm_kernel<{0 if fmt == 'int4_g64' else 1},{nt}>"
+
+
+def time_layer(lay, x, y, M, steps, warmup):
+    """ms per step (quantize + GEMM) by wall clock over `steps` steps, and the GEMM's average
+    launch time by HIP events on the launch stream (a separate pass)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    acts = lay.act_buffers(M)
+    for _ in range(warmup):
+        lay.quantize(x)
+        lay.gemm(acts, M, y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        lay.quantize(x)
+        lay.gemm(acts, M, y)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        lay.quantize(x)
+        e[0].record(stream)
+        lay.gemm(acts, M, y)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return ms, float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
 
 
 def traffic_from_profile(kernel_src: str):
@@ -136,6 +170,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="flux_qkv")
     ap.add_argument("--batch", type=int, default=0, help="rows of X for the mxfp4 sweep (default: all)")
+    ap.add_argument("--format", default="", choices=["", "int4_g64", "mxfp4_b32", "w8a8"],
+                    help="run the workload's layer in another format (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the rank-0 (plain W4A4) comparison run")
@@ -157,6 +193,8 @@ def main():
     d = synth.workload(args.workload)
     if args.batch:
         d = dict(d, x=d["x"][: args.batch], M=args.batch)
+    if args.format:
+        d = dict(d, fmt=args.format)
     M, K, N, r, fmt = d["x"].shape[0], d["K"], d["N"], d["rank"], d["fmt"]
     log(f"[bench] {args.workload}: M={M} K={K} N={N} r={r} fmt={fmt}")
 
@@ -227,15 +265,15 @@ def main():
     peak = PEAK_TOPS[fmt]
     qbytes = quantize_bytes(M, K, r, fmt)
     traffic = traffic_from_profile(os.path.join(ROOT, "w4a4_quantized_gemm_smooth_amd", "csrc", "w4a4_device.hip")) \
-        if args.workload == "flux_qkv" else None
+        if args.workload == "flux_qkv" and fmt == "int4_g64" else None
     out = {
         "metric": "effective TOPS of fused W4A4+rank-32 linear at FLUX shapes; % MFMA peak",
         "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "event_ms_per_step": round(ev_ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4" if fmt == "int4_g64" else "fp4", "data": "synthetic (seeded FLUX-shaped layer; random weights)",
+        "dtype": DTYPE[fmt], "data": "synthetic (seeded FLUX-shaped layer; random weights)",
         "config": {"workload": args.workload, "M": M, "K": K, "N": N, "rank": r, "format": fmt,
                    "ops_per_step": ops, "peak_frac_of_step": round(value / peak, 4)},
-        "roofline": {"bound": "mfma", "kernel": f"gemm_kernel<{0 if fmt == 'int4_g64' else 1},{prep['rank_pad'] // 16}>",
+        "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(fmt, prep["rank_pad"]),
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "avg_launch_ms": round(g_avg, 5), "algorithmic_ops_per_launch": ops},
@@ -281,6 +319,15 @@ def main():
                            "unfused_ms_per_step": round(msu, 5),
                            "unfused_lowrank_overhead_pct": round(100.0 * (msu - ms0) / ms0, 2)}
         del layer0, acts0, layer_u, acts_u, l1s, l2
+        if fmt != "w8a8":
+            # the 8-bit setting (App. D: per-token / per-channel INT8) on the same layer and factors
+            prep8 = w4.prepare_weights(d["w"], lam, r, "w8a8", prep["l1"], prep["l2"])
+            layer8 = w4.W4A4Linear(prep8, inv, device=dev)
+            ms8, g8 = time_layer(layer8, x, y, M, args.steps, args.warmup)
+            out["ablation"].update({"w8a8_ms_per_step": round(ms8, 5), "w8a8_gemm_avg_ms": round(g8, 5),
+                                    "w8a8_gemm_TOPS": round(ops / (g8 * 1e-3) / 1e12, 2),
+                                    "speedup_vs_w8a8": round(ms8 / ms_step, 3)})
+            del layer8, prep8
     if args.copy_calibration:
         n = args.copy_calibration << 18   # float32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)

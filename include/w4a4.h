@@ -44,6 +44,7 @@ extern "C" {
 #define W4A4_ROW_ALIGN 256   /* M and N are padded to a multiple of this in library layouts */
 #define W4A4_RANK_ALIGN 16   /* rank is zero-padded to a multiple of this (r_pad) */
 #define W4A4_MAX_RANK 128    /* largest supported rank (after any LoRA merge) */
+#define W4A4_W8A8_MAX_K 131072 /* W8A8: 127 * 127 * K stays below 2^31 (exact int32 sums) */
 
 typedef enum {
   W4A4_OK = 0,
@@ -55,7 +56,9 @@ typedef enum {
 
 typedef enum {
   W4A4_FMT_INT4_G64 = 0,     /* per-group-64 symmetric INT4, bf16 scales */
-  W4A4_FMT_MXFP4_B32 = 1     /* E2M1 codes, E8M0 scale per block of 32 */
+  W4A4_FMT_MXFP4_B32 = 1,    /* E2M1 codes, E8M0 scale per block of 32 */
+  W4A4_FMT_W8A8 = 2          /* 8-bit setting (App. D): symmetric INT8 per row (activations per
+                                token, weights per output channel), fp32 scales */
 } w4a4_fmt_t;
 
 /* Same object as hipStream_t; NULL is the default stream. */
@@ -72,7 +75,7 @@ int w4a4_abi_version(void);
 const char* w4a4_status_str(w4a4_status_t status);
 
 /*
- * Buffer sizes and layouts. K must be a positive multiple of 64 for both formats (the MXFP4
+ * Buffer sizes and layouts. K must be a positive multiple of 64 for every format (the MXFP4
  * kernels step K by two 32-blocks). m_pad = roundup(M, 256), n_pad = roundup(N, 256),
  * rank_pad = roundup(rank, 16) (0 for rank 0). Layouts (G64 = K/64, B32 = K/32):
  *   wq     [G64][n_pad][32] bytes : the 64 codes of (row, group), 4 bits each.
@@ -85,9 +88,13 @@ const char* w4a4_status_str(w4a4_status_t status);
  *            are zero, which leaves room for o1 in o0 and o2.) The GEMM unfolds this into FP6
  *            MFMA operands with four AND / AND-OR operations per 16 codes.
  *   wscale INT4: [G64][n_pad] bf16;  MXFP4: [B32][n_pad] E8M0 bytes (e + 127)
+ *   W8A8:  wq [B32][n_pad][32] int8 codes (code k of the 32-slice at byte k);
+ *          wscale [n_pad] fp32 (one scale per output channel)
  *   l1t    [rank_pad][K] bf16   : L1ᵀ, rows >= rank are zero
  *   l2t    [n_pad][rank_pad] bf16 : L2ᵀ, columns >= rank are zero
- *   xq, xscale : as wq, wscale with m_pad rows
+ *   xq, xscale : as wq, wscale with m_pad rows. W8A8: xscale holds the [m_pad] fp32 per-token
+ *          scales first; the rest of the buffer is scratch for w4a4_quantize_act (per-K-slice
+ *          partial row maxima).
  *   xl1    fp32, first [m_pad][rank_pad] : t = bf16(X̂)·L1 (fp32 accumulation); the rest of the
  *          buffer (when the size returned here exceeds m_pad·rank_pad·4 bytes) is scratch that
  *          w4a4_quantize_act uses for per-K-slice partial sums of t. 0 bytes when rank == 0.
@@ -165,12 +172,13 @@ w4a4_status_t w4a4_append_lowrank(const uint16_t* l1t, const uint16_t* l2t, int 
 
 /*
  * Library code layout -> canonical: out [rows][K/2] bytes, code 2i in the low nibble; INT4
- * codes become two's-complement nibbles, MXFP4 codes stay E2M1. `q` is a wq or xq buffer
- * (host copy) with roundup(rows, 256) padded rows.
+ * codes become two's-complement nibbles, MXFP4 codes stay E2M1; W8A8: out [rows][K] int8.
+ * `q` is a wq or xq buffer (host copy) with roundup(rows, 256) padded rows.
  */
 w4a4_status_t w4a4_codes_to_canonical(const uint8_t* q, int rows, int K, int fmt, uint8_t* out);
 
-/* Library scale layout -> canonical: INT4 out [rows][K/64] bf16; MXFP4 out [rows][K/32] bytes. */
+/* Library scale layout -> canonical: INT4 out [rows][K/64] bf16; MXFP4 out [rows][K/32] bytes;
+ * W8A8 out [rows] fp32. */
 w4a4_status_t w4a4_scales_to_canonical(const void* s, int rows, int K, int fmt, void* out);
 
 /* ----------------------------------------------------- device (asynchronous on `stream`) */
@@ -180,7 +188,8 @@ w4a4_status_t w4a4_scales_to_canonical(const void* s, int rows, int K, int fmt, 
  * quantizer). Per row m and group:
  *   X̂ = fp32(X · inv_lambda) (one fp32 multiply); codes and scales of X̂ per `fmt`
  *   (INT4: s = bf16(max|X̂|/7), q = rint(X̂ · (1/s)); MXFP4: e = min{e : 6·2^e >= max|X̂|},
- *   E2M1 round-half-even of X̂ / 2^e); t = bf16(X̂) · L1 accumulated in fp32.
+ *   E2M1 round-half-even of X̂ / 2^e; W8A8, per row over all of K: s = fp32(max|X̂|/127),
+ *   q = clamp(rint(X̂ · (1/s)), -127, 127)); t = bf16(X̂) · L1 accumulated in fp32.
  *   X          [M][ldx] bf16 device, ldx >= K, ldx % 8 == 0
  *   inv_lambda [K] fp32 device
  *   l1t        [rank_pad][K] bf16 device (NULL allowed when rank == 0)
@@ -195,6 +204,8 @@ w4a4_status_t w4a4_quantize_act(const uint16_t* X, int M, int K, int ldx, const 
  * The fused 4-bit GEMM with the low-rank up projection in its epilogue (§4.3):
  *   Y[m][n] = bf16( Σ_g s_x[m,g] s_w[n,g] Σ_{k∈g} q_x[m,k] q_w[n,k]      (INT4)
  *                   or Σ_b 2^(e_x+e_w) Σ_{k∈b} val(c_x) val(c_w)          (MXFP4)
+ *                   or s_x[m] s_w[n] Σ_k q_x[m,k] q_w[n,k]                 (W8A8, App. D;
+ *                      exact int32 sum, then fp32; requires K <= 131072)
  *                 + Σ_i bf16(t[m][i]) · L2[i][n]  + bias[n] )
  *   xq, xscale, xl1  outputs of w4a4_quantize_act (device)
  *   wq, wscale, l2t  outputs of w4a4_prepare_weights, copied to the device

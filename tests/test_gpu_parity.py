@@ -72,6 +72,13 @@ def check_activation_side(d, inv, ref_prep, fmt, g, rows=None):
     if fmt == "int4_g64":
         assert np.array_equal(codes, O.pack_int4(act["cx"])), "activation codes differ"
         assert np.array_equal(scales, O.f32_to_bf16_bits(act["sx"])), "activation scales differ"
+    elif fmt == "w8a8":
+        assert np.array_equal(codes, act["cx"]), "activation codes differ"
+        assert np.array_equal(scales, act["sx"]), "activation scales differ"
+        # padding rows: zero codes, zero scales
+        mp = (M + 255) // 256 * 256
+        assert not g["xq"].view(np.int8).reshape(K // 32, mp, 32)[:, M:].any()
+        assert not g["xscale"].view(np.float32)[M:mp].any()
     else:
         assert np.array_equal(codes, O.pack_nibbles(act["cx"])), "activation codes differ"
         assert np.array_equal(scales, act["sx"]), "activation scales differ"
@@ -98,7 +105,7 @@ def oracle_rows(d, inv, ref_prep, fmt, rows, bias=None):
 
 
 # ------------------------------------------------------------------------------- small cases
-@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32"])
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
 def test_tiny_layer(fmt):
     d = synth.workload("tiny")
     lam, inv = _smooth(d)
@@ -110,7 +117,7 @@ def test_tiny_layer(fmt):
     assert np.all(g["y"][:, 256:] == -7.0), "wrote outside the M x N block"
 
 
-@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32"])
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
 @pytest.mark.parametrize("shape", [(200, 320, 300, 20), (1, 64, 7, 0), (257, 128, 513, 48), (130, 192, 129, 5)])
 def test_ragged_shapes_with_bias(fmt, shape):
     m, k, n, r = shape
@@ -148,7 +155,7 @@ def test_zero_and_tiny_activations():
     x[5, :64] = synth.f32_to_bf16_bits(np.full(64, 1e-39, np.float32))
     d = dict(d, x=x)
     lam, inv = _smooth(d)
-    for fmt in ("int4_g64", "mxfp4_b32"):
+    for fmt in ("int4_g64", "mxfp4_b32", "w8a8"):
         ref = oracle_weights(d, 8, fmt, lam)
         g = gpu_layer(d, lam, inv, 8, fmt, ref)
         check_activation_side(d, inv, ref, fmt, g)
@@ -168,7 +175,7 @@ def test_deterministic_and_stream():
         assert np.array_equal(g1[k], g2[k]), k
 
 
-@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32"])
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
 @pytest.mark.parametrize("case", [
     (2000, 512, 8440, 20, True),   # 8 x 33 = 264 tiles (more than the GPU runs at once), 8 groups
     (2000, 832, 8440, 20, True),   # 13 groups: the last ring round is partial
@@ -220,6 +227,23 @@ def test_full_size_int4(name):
     check_activation_side(d, inv, ref, d["fmt"], g)
     rows = _sample_rows(d["M"])
     check_y(g, oracle_rows(d, inv, ref, d["fmt"], rows), rows)
+
+
+def test_full_size_w8a8():
+    """The 8-bit setting (App. D) on the FLUX QKV shapes: all activation codes and per-token
+    scales bit-exact, the weight codes bit-exact, Y on sampled rows."""
+    d, lam, inv, _ = _full("flux_qkv")
+    key = ("flux_qkv", "w8a8")
+    if key not in _CACHE:
+        _CACHE[key] = oracle_weights(d, d["rank"], "w8a8", lam)
+    ref = _CACHE[key]
+    print(f"[flux_qkv w8a8] M={d['M']} K={d['K']} N={d['N']} r={d['rank']}", flush=True)
+    g = gpu_layer(d, lam, inv, d["rank"], "w8a8", ref)
+    wcodes = w4.codes_to_canonical(g["prep"]["wq"], d["N"], d["K"], "w8a8")
+    assert np.array_equal(wcodes, ref["cw"])
+    check_activation_side(d, inv, ref, "w8a8", g)
+    rows = _sample_rows(d["M"], seed=5)
+    check_y(g, oracle_rows(d, inv, ref, "w8a8", rows), rows)
 
 
 def test_full_size_lora_merge():

@@ -42,12 +42,15 @@ def test_buffer_sizes():
     s = w4.buffer_sizes(1000, 300, 128, 20, w4.FMT_MXFP4_B32)
     assert (s["m_pad"], s["n_pad"], s["rank_pad"]) == (1024, 512, 32)
     assert s["wscale"] == 4 * 512 and s["xscale"] == 4 * 1024 and s["l1t"] == 32 * 128 * 2
+    s = w4.buffer_sizes(4608, 9216, 3072, 32, w4.FMT_W8A8)
+    assert s["wq"] == 9216 * 3072 and s["wscale"] == 9216 * 4 and s["xq"] == 4608 * 3072
+    assert s["xscale"] >= 4608 * 4 * 2 and s["xscale"] % (4608 * 4) == 0   # scales + partial maxima
 
 
 @pytest.mark.parametrize("args,status", [
     ((0, 10, 64, 0, 0), 1), ((10, 0, 64, 0, 0), 1), ((10, 10, 96, 0, 0), 1), ((10, 10, 0, 0, 0), 1),
     ((10, 10, 64, 11, 0), 1), ((10, 200, 64, 65, 0), 1), ((10, 10, 64, -1, 0), 1), ((300, 300, 256, 129, 0), 1),
-    ((10, 10, 64, 0, 7), 2),
+    ((10, 10, 64, 0, 7), 2), ((10, 10, w4.W8A8_MAX_K + 64, 0, 2), 1),
 ])
 def test_buffer_sizes_rejects(args, status):
     s = w4._Sizes()
@@ -90,7 +93,7 @@ def _oracle_prep(d, rank, fmt):
 
 
 @pytest.mark.parametrize("shape", [(128, 256, 256, 16), (70, 320, 200, 8), (33, 64, 300, 0), (20, 192, 130, 48)])
-@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32"])
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
 def test_weight_codes_bit_exact_given_oracle_factors(shape, fmt):
     m, k, n, r = shape
     d = synth.make_layer(m, k, n, n_outliers=max(1, k // 64), outlier_scale=40.0, seed=11 + k + n)
@@ -102,6 +105,8 @@ def test_weight_codes_bit_exact_given_oracle_factors(shape, fmt):
     if fmt == "int4_g64":
         assert np.array_equal(codes, O.pack_int4(ref["cw"]))
         assert np.array_equal(scales, O.f32_to_bf16_bits(ref["sw"]))
+    elif fmt == "w8a8":
+        assert np.array_equal(codes, ref["cw"]) and np.array_equal(scales, ref["sw"])
     else:
         assert np.array_equal(codes, O.pack_nibbles(ref["cw"]))
         assert np.array_equal(scales, ref["sw"])
@@ -112,7 +117,7 @@ def test_weight_codes_bit_exact_given_oracle_factors(shape, fmt):
         assert np.array_equal(l1t[:r].T, l1b) and not l1t[r:].any()
         assert np.array_equal(l2t[:n, :r].T, l2b) and not l2t[:, r:].any() and not l2t[n:].any()
     # padding rows are zero codes with zero scales
-    wq = prep["wq"].reshape(k // 64, prep["n_pad"], 32)
+    wq = prep["wq"].reshape(k // (32 if fmt == "w8a8" else 64), prep["n_pad"], 32)
     assert not wq[:, n:].any()
 
 
@@ -147,6 +152,13 @@ def test_padding_and_layout_of_weight_codes():
     qm, _ = O.quant_mxfp4_b32(O.bf16_bits_to_f32(d["w"]))
     raw = prep["wq"].reshape(1, 256, 32)[0, :3]
     assert np.array_equal(raw & 0xF, qm[:, 0::2]) and np.array_equal(raw >> 4, qm[:, 1::2])
+    # W8A8: [K/32][n_pad][32] int8 codes, fp32 per-row scales [n_pad]
+    prep = w4.prepare_weights(d["w"], lam, 0, "w8a8")
+    q8, s8 = O.quant_int8_rows(O.bf16_bits_to_f32(d["w"]))
+    raw = prep["wq"].view(np.int8).reshape(2, 256, 32)
+    assert np.array_equal(np.concatenate([raw[0, :3], raw[1, :3]], axis=1), q8) and not raw[:, 3:].any()
+    sc = prep["wscale"].view(np.float32)
+    assert np.array_equal(sc[:3], s8) and not sc[3:].any()
 
 
 def _lowrank_err(w_hat, l1_bits, l2_bits):
@@ -200,6 +212,11 @@ def _split_error_of(prep, w_bits, lam, fmt):
     """The oracle's split error of a library preparation (codes and scales decoded canonically)."""
     n, k = w_bits.shape
     canon = w4.codes_to_canonical(prep["wq"], n, k, fmt)
+    w_hat = O.smooth_weights(O.bf16_bits_to_f32(w_bits), lam)
+    l1 = O.bf16_bits_to_f32(prep["l1"])
+    l2 = O.bf16_bits_to_f32(prep["l2"])
+    if fmt == "w8a8":
+        return O.split_error(w_hat, l1, l2, canon, w4.scales_to_canonical(prep["wscale"], n, k, fmt), fmt)
     lo, hi = canon & 0xF, canon >> 4
     nib = np.empty((n, k), np.uint8)
     nib[:, 0::2], nib[:, 1::2] = lo, hi
@@ -209,13 +226,10 @@ def _split_error_of(prep, w_bits, lam, fmt):
         scales = O.bf16_bits_to_f32(sc)
     else:
         codes, scales = nib, sc
-    w_hat = O.smooth_weights(O.bf16_bits_to_f32(w_bits), lam)
-    l1 = O.bf16_bits_to_f32(prep["l1"])
-    l2 = O.bf16_bits_to_f32(prep["l2"])
     return O.split_error(w_hat, l1, l2, codes, scales, fmt)
 
 
-@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32"])
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
 def test_refined_split(fmt):
     """Iterative refinement (§4.2): iteration 0 is the plain preparation byte for byte; the kept
     iteration's arrays reproduce its reported score (recomputed by the oracle) and have the

@@ -26,12 +26,14 @@ __all__ = [
 
 FMT_INT4_G64 = 0
 FMT_MXFP4_B32 = 1
+FMT_W8A8 = 2
 GROUP = 64
 MX_BLOCK = 32
 ROW_ALIGN = 256
 RANK_ALIGN = 16
 MAX_RANK = 128
-_FMT_NAMES = {"int4_g64": FMT_INT4_G64, "mxfp4_b32": FMT_MXFP4_B32}
+W8A8_MAX_K = 131072
+_FMT_NAMES = {"int4_g64": FMT_INT4_G64, "mxfp4_b32": FMT_MXFP4_B32, "w8a8": FMT_W8A8}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libw4a4.so")
@@ -192,15 +194,25 @@ def append_lowrank(l1t: np.ndarray, l2t: np.ndarray, K: int, N: int, rank: int, 
 
 
 def codes_to_canonical(q: np.ndarray, rows: int, K: int, fmt=FMT_INT4_G64) -> np.ndarray:
-    out = np.empty((rows, K // 2), np.uint8)
-    _check("w4a4_codes_to_canonical", lib().w4a4_codes_to_canonical(_hptr(_c(q, np.uint8)), rows, K, _fmt(fmt), _hptr(out)))
+    """[rows][K/2] packed nibbles (INT4, MXFP4) or [rows][K] int8 (W8A8)."""
+    w8 = _fmt(fmt) == FMT_W8A8
+    out = np.empty((rows, K), np.int8) if w8 else np.empty((rows, K // 2), np.uint8)
+    src = np.ascontiguousarray(q).view(np.uint8)
+    _check("w4a4_codes_to_canonical", lib().w4a4_codes_to_canonical(_hptr(src), rows, K, _fmt(fmt), _hptr(out)))
     return out
 
 
 def scales_to_canonical(s: np.ndarray, rows: int, K: int, fmt=FMT_INT4_G64) -> np.ndarray:
+    """INT4 [rows][K/64] bf16 bits; MXFP4 [rows][K/32] E8M0 bytes; W8A8 [rows] fp32."""
     f = _fmt(fmt)
-    out = np.empty((rows, K // GROUP), np.uint16) if f == FMT_INT4_G64 else np.empty((rows, K // MX_BLOCK), np.uint8)
-    _check("w4a4_scales_to_canonical", lib().w4a4_scales_to_canonical(_hptr(_c(s, np.uint8).view(np.uint8)), rows, K, f, _hptr(out)))
+    if f == FMT_W8A8:
+        out = np.empty(rows, np.float32)
+    elif f == FMT_INT4_G64:
+        out = np.empty((rows, K // GROUP), np.uint16)
+    else:
+        out = np.empty((rows, K // MX_BLOCK), np.uint8)
+    src = np.ascontiguousarray(s).view(np.uint8)  # raw bytes of the library buffer
+    _check("w4a4_scales_to_canonical", lib().w4a4_scales_to_canonical(_hptr(src), rows, K, f, _hptr(out)))
     return out
 
 

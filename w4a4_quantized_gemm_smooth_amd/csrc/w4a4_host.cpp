@@ -167,6 +167,21 @@ void quant_mxfp4_chunk(const float* v, uint8_t* out32, uint8_t* e8_lo, uint8_t* 
   for (int i = 0; i < W4A4_GROUP / 2; ++i) out32[i] = uint8_t(nib[2 * i] | (nib[2 * i + 1] << 4));
 }
 
+// 8-bit setting: one symmetric INT8 scale per row, s = fp32(max|v| / 127) (zero below 2^-126),
+// q = clamp(rint(fp32(v * fp32(1/s))), -127, 127). Codes go to q8[k], k = 0 .. K-1.
+float quant_int8_row(const float* v, int K, int8_t* q8) {
+  float amax = 0.0f;
+  for (int k = 0; k < K; ++k) amax = std::max(amax, std::fabs(v[k]));
+  float s = amax / 127.0f;
+  if (!(s >= 0x1p-126f)) s = 0.0f;
+  const float inv = s != 0.0f ? 1.0f / s : 0.0f;
+  for (int k = 0; k < K; ++k) {
+    const float y = v[k] * inv;
+    q8[k] = int8_t(std::min(127, std::max(-127, int(std::nearbyint(y)))));
+  }
+  return s;
+}
+
 // ------------------------------------------------------------------------------ own SVD
 // Truncated SVD of Ŵᵀ (Ŵ is [N][K] row-major, fp64) by randomized subspace iteration
 // (Halko, Martinsson & Tropp 2011, Alg. 4.4) followed by a one-sided Jacobi SVD (Hestenes) of
@@ -378,14 +393,15 @@ bool split_once(const std::vector<double>& what, const double* target, int N, in
   for (size_t i = 0; i < L1.size(); ++i) l1d[i] = bf16_to_f32(L1[i]);
   for (size_t i = 0; i < L2.size(); ++i) l2d[i] = bf16_to_f32(L2[i]);
   // residual and its quantization, one weight row per task
-  const bool mx = fmt == W4A4_FMT_MXFP4_B32;
-  std::memset(wq, 0, size_t(np) * K / 2);
-  std::memset(wscale, 0, mx ? size_t(K / W4A4_MX_BLOCK) * np : size_t(G) * np * 2);
+  const bool mx = fmt == W4A4_FMT_MXFP4_B32, w8 = fmt == W4A4_FMT_W8A8;
+  std::memset(wq, 0, w8 ? size_t(np) * K : size_t(np) * K / 2);
+  std::memset(wscale, 0, w8 ? size_t(np) * 4 : mx ? size_t(K / W4A4_MX_BLOCK) * np : size_t(G) * np * 2);
   if (deq) deq->assign(size_t(N) * K, 0.0);
   std::vector<double> row_err(static_cast<size_t>(N), 0.0);
   parallel_for(N, [&](int b, int e, int) {
     std::vector<float> rrow(static_cast<size_t>(K));
     std::vector<double> lrow(static_cast<size_t>(K));
+    std::vector<int8_t> q8(w8 ? size_t(K) : 0);
     for (int n = b; n < e; ++n) {
       for (int k = 0; k < K; ++k) {
         double d = 0.0;
@@ -394,6 +410,20 @@ bool split_once(const std::vector<double>& what, const double* target, int N, in
         rrow[k] = float(what[size_t(n) * K + k] - d);
       }
       double acc = 0.0;
+      if (w8) {  // codes [K/32][np][32], one fp32 scale per output channel
+        const float s = quant_int8_row(rrow.data(), K, q8.data());
+        static_cast<float*>(wscale)[n] = s;
+        for (int k = 0; k < K; ++k) {
+          wq[(size_t(k / 32) * np + n) * 32 + k % 32] = uint8_t(q8[k]);
+          const size_t idx = size_t(n) * K + k;
+          const double v = double(q8[k]) * double(s);
+          if (deq) (*deq)[idx] = v;
+          const double miss = what[idx] - lrow[k] - v;
+          acc += miss * miss;
+        }
+        row_err[n] = acc;
+        continue;
+      }
       for (int g = 0; g < G; ++g) {
         uint8_t* dst = wq + (size_t(g) * np + n) * 32;
         double v[W4A4_GROUP];
@@ -495,12 +525,13 @@ w4a4_status_t w4a4_buffer_sizes(int M, int N, int K, int rank, int fmt, w4a4_siz
   out->m_pad = int(mp);
   out->n_pad = int(np);
   out->rank_pad = int(rp);
-  out->wq = np * kk / 2;
-  out->wscale = mx ? (kk / W4A4_MX_BLOCK) * np : (kk / W4A4_GROUP) * np * 2;
+  const bool w8 = fmt == W4A4_FMT_W8A8;
+  out->wq = w8 ? np * kk : np * kk / 2;
+  out->wscale = w8 ? np * 4 : mx ? (kk / W4A4_MX_BLOCK) * np : (kk / W4A4_GROUP) * np * 2;
   out->l1t = rp * kk * 2;
   out->l2t = np * rp * 2;
-  out->xq = mp * kk / 2;
-  out->xscale = mx ? (kk / W4A4_MX_BLOCK) * mp : (kk / W4A4_GROUP) * mp * 2;
+  out->xq = w8 ? mp * kk : mp * kk / 2;
+  out->xscale = w8 ? w8_xscale_floats(M, K) * 4 : mx ? (kk / W4A4_MX_BLOCK) * mp : (kk / W4A4_GROUP) * mp * 2;
   out->xl1 = xl1_floats(M, K, rank) * 4;
   return W4A4_OK;
 }
@@ -571,8 +602,9 @@ w4a4_status_t w4a4_prepare_weights_refined(const uint16_t* W, int N, int K, cons
   if (iters < 0 || iters > 64) return W4A4_ERR_INVALID_ARG;
   try {
     const int np = rows_pad_of(N), G = K / W4A4_GROUP;
-    const bool mx = fmt == W4A4_FMT_MXFP4_B32;
-    const size_t q_bytes = size_t(np) * K / 2, s_bytes = mx ? size_t(K / W4A4_MX_BLOCK) * np : size_t(G) * np * 2;
+    const bool mx = fmt == W4A4_FMT_MXFP4_B32, w8 = fmt == W4A4_FMT_W8A8;
+    const size_t q_bytes = w8 ? size_t(np) * K : size_t(np) * K / 2;
+    const size_t s_bytes = w8 ? size_t(np) * 4 : mx ? size_t(K / W4A4_MX_BLOCK) * np : size_t(G) * np * 2;
     const std::vector<double> what = smoothed_weight(W, N, K, lambda);
     std::vector<double> target = what, deq;
     std::vector<uint8_t> q(q_bytes), sc(s_bytes);
@@ -629,6 +661,11 @@ w4a4_status_t w4a4_codes_to_canonical(const uint8_t* q, int rows, int K, int fmt
   if (!fmt_known(fmt)) return W4A4_ERR_UNSUPPORTED;
   if (!q || !out || rows < 1 || K < W4A4_GROUP || K % W4A4_GROUP) return W4A4_ERR_INVALID_ARG;
   const int rp = rows_pad_of(rows), G = K / W4A4_GROUP;
+  if (fmt == W4A4_FMT_W8A8) {
+    for (int r = 0; r < rows; ++r)
+      for (int b = 0; b < K / 32; ++b) std::memcpy(out + size_t(r) * K + size_t(b) * 32, q + (size_t(b) * rp + r) * 32, 32);
+    return W4A4_OK;
+  }
   for (int r = 0; r < rows; ++r)
     for (int g = 0; g < G; ++g) {
       const uint8_t* src = q + (size_t(g) * rp + r) * 32;
@@ -648,7 +685,9 @@ w4a4_status_t w4a4_scales_to_canonical(const void* s, int rows, int K, int fmt, 
   if (!fmt_known(fmt)) return W4A4_ERR_UNSUPPORTED;
   if (!s || !out || rows < 1 || K < W4A4_GROUP || K % W4A4_GROUP) return W4A4_ERR_INVALID_ARG;
   const int rp = rows_pad_of(rows);
-  if (fmt == W4A4_FMT_INT4_G64) {
+  if (fmt == W4A4_FMT_W8A8) {
+    std::memcpy(out, s, size_t(rows) * 4);
+  } else if (fmt == W4A4_FMT_INT4_G64) {
     const int G = K / W4A4_GROUP;
     const uint16_t* src = static_cast<const uint16_t*>(s);
     uint16_t* dst = static_cast<uint16_t*>(out);

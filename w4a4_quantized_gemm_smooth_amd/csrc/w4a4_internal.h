@@ -13,13 +13,20 @@ inline int round_up(int x, int a) { return (x + a - 1) / a * a; }
 inline int rank_pad_of(int rank) { return round_up(rank, W4A4_RANK_ALIGN); }
 inline int rows_pad_of(int rows) { return round_up(rows, W4A4_ROW_ALIGN); }
 
-inline bool fmt_known(int fmt) { return fmt == W4A4_FMT_INT4_G64 || fmt == W4A4_FMT_MXFP4_B32; }
+inline bool fmt_known(int fmt) {
+  return fmt == W4A4_FMT_INT4_G64 || fmt == W4A4_FMT_MXFP4_B32 || fmt == W4A4_FMT_W8A8;
+}
 
 // Shared shape checks: M, N >= 1; K a positive multiple of 64; 0 <= rank <= min(N, K, MAX).
 inline w4a4_status_t check_shape(int M, int N, int K, int rank, int fmt) {
   if (!fmt_known(fmt)) return W4A4_ERR_UNSUPPORTED;
   if (M < 1 || N < 1 || K < W4A4_GROUP || K % W4A4_GROUP != 0) return W4A4_ERR_INVALID_ARG;
   if (rank < 0 || rank > W4A4_MAX_RANK || rank > N || rank > K) return W4A4_ERR_INVALID_ARG;
+  // W8A8: the int32 dot product of 127-bounded codes must not overflow, and the one-byte codes
+  // (rows_pad * K bytes per operand) must stay below 2^31 bytes
+  if (fmt == W4A4_FMT_W8A8 && (K > W4A4_W8A8_MAX_K || (long long)rows_pad_of(M) * K >= (1LL << 31) ||
+                               (long long)rows_pad_of(N) * K >= (1LL << 31)))
+    return W4A4_ERR_INVALID_ARG;
   // sizes must stay addressable with 32-bit element offsets inside the kernels
   if ((long long)rows_pad_of(M) * K > (1LL << 31) || (long long)rows_pad_of(N) * K > (1LL << 31))
     return W4A4_ERR_INVALID_ARG;
@@ -53,6 +60,10 @@ inline size_t xl1_floats(int M, int K, int rank) {
   const int ks = qa_slices(M, K);
   return rank == 0 ? 0 : (ks > 1 ? t * size_t(1 + ks) : t);
 }
+
+// floats of a W8A8 xscale buffer: the [m_pad] per-token scales, then one [m_pad] plane of partial
+// row maxima per slice (written by the first activation kernel, reduced by the second)
+inline size_t w8_xscale_floats(int M, int K) { return size_t(rows_pad_of(M)) * size_t(1 + qa_slices(M, K)); }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
