@@ -25,9 +25,13 @@ ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32);
 # -ffp-contract=off: every fp32 step that must be bit-reproducible stays a separate IEEE op.
 DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
-                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                # MFMA results in VGPRs: the group epilogue reads them with plain VALU FMAs
-                "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-I", INCLUDE, "-I", CSRC]
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
+# Per translation unit: the 4-bit kernels keep MFMA results in VGPRs (the group epilogue reads them
+# with plain VALU FMAs); the W8A8 kernels leave the register form of the MFMAs to the compiler.
+DEVICE_SOURCES = {
+    "w4a4_device.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "w4a4_device_w8a8.hip": [],
+}
 HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-pthread", "-I", INCLUDE, "-I", CSRC]
 
 
@@ -45,12 +49,15 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     host_o = os.path.join(BUILD_DIR, "w4a4_host.o")
-    dev_o = os.path.join(BUILD_DIR, "w4a4_device.o")
     cxx = shutil.which("g++") or "g++"
     _run([cxx, *HOST_FLAGS, "-c", os.path.join(CSRC, "w4a4_host.cpp"), "-o", host_o], verbose)
-    _run([HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, "w4a4_device.hip"), "-o", dev_o], verbose)
+    objs = [host_o]
+    for src, extra in DEVICE_SOURCES.items():
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        _run([HIPCC, *DEVICE_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", host_o, dev_o, "-o", tmp], verbose)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

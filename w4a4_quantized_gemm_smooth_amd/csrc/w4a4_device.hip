@@ -22,32 +22,12 @@
 //  * The low-rank branch uses the bf16 MFMAs (16x16x32 for the down projection, 32x32x16 for the
 //    up projection, accumulating straight into the GEMM accumulators).
 
-#include <hip/hip_runtime.h>
-
-#include "w4a4_internal.h"
+#include "w4a4_device_common.h"
 
 using namespace w4a4;
+using namespace w4a4::dev;
 
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef int v6i __attribute__((ext_vector_type(6)));
-
-__device__ __forceinline__ float bf16f(uint32_t h16) { return __uint_as_float(h16 << 16); }
-
-// float -> bf16 bits, nearest-even (finite inputs)
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ v8bf as_bf16x8(v4i v) { return __builtin_bit_cast(v8bf, v); }
 
 // Folded FP6 layout of INT4 codes. A run of 16 codes c_0..c_15 has the FP6 image
 // I = Σ_f (sign_f << 5 | |c_f|) << 6f (96 bits, dwords o0 o1 o2). Bits 3 and 4 of every 6-bit field
@@ -76,19 +56,6 @@ __device__ __forceinline__ v8i unfold_fp6(v4i d) {
 // ===================================================================================
 constexpr int QA_WAVES = QA_BLOCK_ROWS / 16;
 
-// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left alone), visible to the compiler's wait tracking
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {  // v_cvt_pk_bf16_f32, nearest-even
-  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), bf2));
-}
 
 // LDS bytes of one block: 1/λ (16 B slots), L1 rows of RP rank columns padded by one slot, in
 // whole 64-slot DMA instructions
@@ -293,69 +260,6 @@ __global__ __launch_bounds__(256) void t_reduce_kernel(const float* __restrict__
   *reinterpret_cast<float4*>(t + i) = s;
 }
 
-// W8A8 (App. D, per-token INT8): the scale of a row needs max|X̂| over all of K, which the first
-// kernel leaves as one partial maximum per K slice. This kernel reduces them (max is exact in any
-// order), s = fp32(max/127) (zero below 2^-126), and writes q = clamp(rint(X̂ · fp32(1/s)), ±127)
-// with X̂ recomputed from X by the same single fp32 multiply. Block = 16 rows x 1024 K: lane c of a
-// wave owns the 16 values 16 c .. 16 c + 15 of the chunk (1/λ loaded once) and the wave takes rows
-// wave, wave + 4, ... (row-uniform, so the partial maxima are scalar loads). Codes go to the
-// [K/32][m_pad][32] layout as one 16-byte store per lane and row.
-constexpr int Q8_ROWS = 16, Q8_KCHUNK = 1024;
-
-__global__ __launch_bounds__(256) void quantize_w8_kernel(const uint16_t* __restrict__ X, int M, int K, int ldx,
-                                                          const float* __restrict__ inv_lambda, int m_pad, int nsl,
-                                                          uint8_t* __restrict__ xq, float* __restrict__ xscale) {
-  const int nkb = (K + Q8_KCHUNK - 1) / Q8_KCHUNK;
-  const int rb = blockIdx.x / nkb, kb = blockIdx.x % nkb;
-  const int c = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int k = kb * Q8_KCHUNK + 16 * c;
-  const bool kin = k < K;  // K is a multiple of 64: a lane's 16 values are all in or all out
-  float il[16];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 v = kin ? *reinterpret_cast<const float4*>(inv_lambda + k + 4 * q) : float4{0.f, 0.f, 0.f, 0.f};
-    il[4 * q] = v.x;
-    il[4 * q + 1] = v.y;
-    il[4 * q + 2] = v.z;
-    il[4 * q + 3] = v.w;
-  }
-  const float* part = xscale + m_pad;
-#pragma unroll
-  for (int i = 0; i < Q8_ROWS / 4; ++i) {
-    const int row = rb * Q8_ROWS + wave + 4 * i;
-    float amax = 0.f;
-    for (int p = 0; p < nsl; ++p) amax = fmaxf(amax, part[(size_t)p * m_pad + row]);
-    float sc = amax / 127.0f;
-    if (!(sc >= 0x1p-126f)) sc = 0.f;
-    const float inv = sc != 0.f ? 1.0f / sc : 0.f;
-    if (kb == 0 && c == 0) xscale[row] = sc;
-    if (!kin) continue;
-    uint4 xv[2] = {uint4{0u, 0u, 0u, 0u}, uint4{0u, 0u, 0u, 0u}};
-    if (row < M) {
-      const uint4* src = reinterpret_cast<const uint4*>(X + (size_t)row * ldx + k);
-      xv[0] = src[0];
-      xv[1] = src[1];
-    }
-    uint32_t w[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint4 v = xv[d >> 1];
-      const uint32_t x01 = (d & 1) ? v.z : v.x, x23 = (d & 1) ? v.w : v.y;
-      const uint32_t bits[4] = {x01 & 0xFFFFu, x01 >> 16, x23 & 0xFFFFu, x23 >> 16};
-      uint32_t word = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float xh = bf16f(bits[e]) * il[4 * d + e];  // X̂, one fp32 multiply
-        const float y = fminf(127.f, fmaxf(-127.f, __builtin_rintf(xh * inv)));
-        word |= ((uint32_t)(int)y & 0xFFu) << (8 * e);
-      }
-      w[d] = word;
-    }
-    *reinterpret_cast<uint4*>(xq + ((size_t)(k >> 5) * m_pad + row) * 32 + (k & 31)) = uint4{w[0], w[1], w[2], w[3]};
-  }
-}
-
 // ===================================================================================
 // Kernel 2: the 4-bit GEMM + low-rank up projection (+ bias), bf16 out, INT4 or MXFP4.
 //
@@ -370,77 +274,7 @@ __global__ __launch_bounds__(256) void quantize_w8_kernel(const uint16_t* __rest
 //    in place.
 // The epilogue adds bf16(t)·L2 and the bias and writes Y through LDS in 16-byte row segments.
 // ===================================================================================
-constexpr int I4_BM = 256, I4_BN = 256, I4_THREADS = 512;
-constexpr int I4_MT = 4;            // 32-row tiles per wave (M)
-constexpr int I4_GROUP_M = 4;
-constexpr int I4_NS = 8;            // ring slots (groups); even
-
-// LDS swizzle of 32-byte code rows: row r, 16-byte half h (rows 8..15 of every 16 swap halves, so
-// the 16-byte reads of 8 consecutive lanes cover all 64 banks)
-__device__ __forceinline__ int sw_off32(int r, int h) { return r * 32 + 16 * (h ^ ((r >> 3) & 1)); }
-
-// Tile order. Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8),
-// so consecutive logical tiles are handed to the same XCD; logical tiles then sweep N in groups of
-// I4_GROUP_M M-tiles, so the blocks an XCD runs together share A and B slices in its L2.
-__device__ __forceinline__ void tile_of(int b, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int xcd = b & 7, idx = b >> 3, q = nblocks >> 3, rem = nblocks & 7;
-  const int logical = xcd * q + min(xcd, rem) + idx;
-  const int per_group = I4_GROUP_M * tiles_n;
-  const int first_m = (logical / per_group) * I4_GROUP_M;
-  const int gsize = min(tiles_m - first_m, I4_GROUP_M);
-  const int in_group = logical % per_group;
-  tm = first_m + in_group % gsize;
-  tn = in_group / gsize;
-}
-
-// Y store shared by the GEMMs: the wave's 128 x 64 block of fp32 results (+ bias) -> bf16 Y
-// through LDS, so that every lane writes whole 16-byte row segments. The block goes out in two
-// halves of 64 rows, staged in `stage` (an idle ring slot of the wave) with a 144-byte row stride
-// (conflict-free 2-byte writes and 16-byte reads). The 32x32 MFMA output layout: lane holds column
-// lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4. r0, c0: first row and column of the wave's block.
-constexpr int Y_ES = 144;
-__device__ __forceinline__ void store_y(v16f (&acc)[I4_MT][2], uint8_t* stage, const uint16_t* bias, uint16_t* Y,
-                                        int ldy, int M, int N, int r0, int c0, int lane) {
-  const int lr = lane & 31, lh = lane >> 5;
-  const bool vec_ok = ((reinterpret_cast<uintptr_t>(Y) & 15u) == 0) && (ldy % 8 == 0);
-  float bcol[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = c0 + j * 32 + lr;
-    bcol[j] = (bias && col < N) ? bf16f(bias[col]) : 0.f;
-  }
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const int rl = ii * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-          const uint32_t pr = pack_bf16x2(acc[2 * half + ii][j][v] + bcol[j], acc[2 * half + ii][j][v + 1] + bcol[j]);
-          uint16_t* d = reinterpret_cast<uint16_t*>(stage + rl * Y_ES + (j * 32 + lr) * 2);
-          d[0] = (uint16_t)pr;
-          d[Y_ES / 2] = (uint16_t)(pr >> 16);
-        }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int idx = q * 64 + lane, rr = idx >> 3, c = idx & 7;
-      const uint4 val = *reinterpret_cast<const uint4*>(stage + rr * Y_ES + c * 16);
-      const int row = r0 + half * 64 + rr, col = c0 + c * 8;
-      if (row >= M) continue;
-      uint16_t* dst = Y + (size_t)row * ldy + col;
-      if (vec_ok && col + 8 <= N) {
-        *reinterpret_cast<uint4*>(dst) = val;
-      } else {
-        const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (col + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-      }
-    }
-  }
-}
+constexpr int I4_THREADS = 512;
 
 // One ring slot: the folded codes of 256 A rows and 256 B rows (32 B each, swizzled) and their
 // bf16 scales (A rows 0..255, then B rows). Each slot is its own LDS object, so the compiler can
@@ -806,194 +640,6 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   store_y(acc, stage, bias, Y, ldy, M, N, m0 + wm * 128, n0 + wn * 64, lane);
 }
 
-// ===================================================================================
-// Kernel 3: the W8A8 GEMM (App. D's 8-bit setting) on the same block tiling, DMA ring and Y store
-// as the 4-bit GEMM. One K step = 32 codes: a ring slot holds the int8 codes of the block's 256 A
-// rows and 256 B rows (32 B each, swizzled as above). Per step each wave runs one
-// v_mfma_i32_32x32x32_i8 per 32x32 tile into int32 accumulators (exact: |Σ| <= 127² K < 2^31);
-// lane (r, h) supplies bytes 16h .. 16h + 15 of A row r and of B column r, so A and B pair the same
-// k whatever order the unit sums them in. The epilogue converts to fp32, scales by s_x[m] s_w[n],
-// adds bf16(t)·L2 with bf16 MFMAs that accumulate into the scaled values, adds the bias and stores.
-// Up to rank 32 the block's t tile is copied into an LDS area of its own by the DMA path in the
-// prologue (8 slots of 16 KB + 32 KB fill the CU's 160 KB); larger ranks read t from global memory
-// in the epilogue, 32 ranks at a time.
-// ===================================================================================
-struct I8Slot {
-  uint8_t a[256 * 32];
-  uint8_t b[256 * 32];
-};
-
-template <int NTR>  // NTR = rank_pad / 16
-__global__ __launch_bounds__(I4_THREADS) void gemm_w8a8_kernel(
-    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const float* __restrict__ xl1,
-    const uint8_t* __restrict__ wq, const float* __restrict__ ws, const uint16_t* __restrict__ l2t,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K, int m_pad,
-    int n_pad) {
-  constexpr int RP = NTR * 16, KS = 2;
-  constexpr bool T_LDS = NTR > 0 && NTR <= 2;
-  constexpr int TROWB = RP * 4;  // bytes of one t row
-  __shared__ __attribute__((aligned(16))) I8Slot sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7;
-  __shared__ __attribute__((aligned(16))) uint8_t t_tile[T_LDS ? 256 * TROWB : 16];
-  I8Slot* const ring[I4_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5, &sl6, &sl7};
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
-  int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, m_pad / I4_BM, n_pad / I4_BN, tm, tn);
-  const int m0 = tm * I4_BM, n0 = tn * I4_BN;
-  const int S = K / 32;
-
-  // DMA: instruction w of an operand fills bytes [1024 w, 1024 w + 1024) of the slot, lane i the
-  // 16 bytes of row 32 w + i / 2 that the swizzle puts there (2 instructions per wave and step)
-  const int drow = 32 * wave + (lane >> 1);
-  const int dhalf = (lane & 1) ^ ((drow >> 3) & 1);
-  const int c_lane = drow * 32 + 16 * dhalf;
-  constexpr int RSRC_W3 = 0x00020000;
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(xq + (size_t)m0 * 32), 0, (S * m_pad - m0) * 32, RSRC_W3);
-  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(wq + (size_t)n0 * 32), 0, (S * n_pad - n0) * 32, RSRC_W3);
-  typedef __attribute__((address_space(3))) void* lds_ptr;
-  auto dma = [&](int k, I8Slot* sl) {  // steps past the end reload the last step
-    k = min(k, S - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr)(sl->a + 1024 * wave), 16, c_lane, k * m_pad * 32, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr)(sl->b + 1024 * wave), 16, c_lane, k * n_pad * 32, 0, 0);
-  };
-
-  if (T_LDS) {  // t tile -> its LDS area: 256 * TROWB / 8 bytes per wave, 1 KB per DMA instruction
-    const __amdgpu_buffer_rsrc_t t_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(xl1 + (size_t)m0 * RP), 0, (m_pad - m0) * TROWB, RSRC_W3);
-    constexpr int TCHUNK = 256 * TROWB / 8;
-#pragma unroll
-    for (int q = 0; q < TCHUNK / 1024; ++q) {
-      const int off = wave * TCHUNK + q * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr)(t_tile + off), 16, 16 * lane, off, 0, 0);
-    }
-  }
-  // prologue: steps 0 .. NS-3 in flight; the t tile and step 0 visible
-#pragma unroll
-  for (int k = 0; k < I4_NS - 2; ++k) dma(k, ring[k]);
-  wait_vmcnt<2 * (I4_NS - 3)>();
-  __builtin_amdgcn_s_barrier();
-
-  const int lr = lane & 31, lh = lane >> 5;
-  const int arow0 = wm * 128 + lr, bcol0 = wn * 64 + lr;
-  const int a_off = sw_off32(arow0, lh), b_off = sw_off32(bcol0, lh);
-  auto a_raw = [&](const I8Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i); };
-  auto b_raw = [&](const I8Slot* sl, int j) { return *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j); };
-  // operands of step k + 1 are read at the start of step k (double-buffered registers); steps past
-  // the end read their stale slot and have B forced to zero codes after this step's MFMAs (so the
-  // select does not wait for the reads early), adding exactly 0
-  auto rd = [&](const I8Slot* sl, v4i (&A)[I4_MT], v4i (&B)[2]) {
-#pragma unroll
-    for (int i = 0; i < I4_MT; ++i) A[i] = a_raw(sl, i);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) B[j] = b_raw(sl, j);
-  };
-  v16i acc[I4_MT][2];
-#pragma unroll
-  for (int i = 0; i < I4_MT; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
-  v4i A[2][I4_MT], B[2][2];
-  rd(ring[0], A[0], B[0]);
-  for (int k0 = 0; k0 < S; k0 += I4_NS) {
-#pragma unroll
-    for (int u = 0; u < I4_NS; ++u) {
-      const int k = k0 + u, c = u & 1;
-      if (u % 2 == 0) {
-        // steps k+1 and k+2 have landed in every wave's share of their slots; everyone is done with
-        // slots k-2 and k-1, which take steps k+NS-2 and k+NS-1
-        wait_vmcnt<2 * (I4_NS - 5)>();
-        __builtin_amdgcn_s_barrier();
-        dma(k + I4_NS - 2, ring[(u + I4_NS - 2) % I4_NS]);
-        dma(k + I4_NS - 1, ring[(u + I4_NS - 1) % I4_NS]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      rd(ring[(u + 1) % I4_NS], A[c ^ 1], B[c ^ 1]);
-      __builtin_amdgcn_sched_barrier(0);  // the next step's reads stay ahead of this step's MFMAs
-#pragma unroll
-      for (int t = 0; t < 2 * I4_MT; ++t) {
-        const int i = t >> 1, j = t & 1;
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[c][i], B[c][j], acc[i][j], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      const bool live = k + 1 < S;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) B[c ^ 1][j] = live ? B[c ^ 1][j] : v4i{0, 0, 0, 0};
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  wait_vmcnt<0>();  // no LDS DMA may outlive the block
-  __builtin_amdgcn_s_barrier();
-
-  // ---- epilogue: fp32 = int32 · (s_x[m] s_w[n]); then + bf16(t)·L2, + bias
-  v16f out[I4_MT][2];
-  float swc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) swc[j] = ws[n0 + bcol0 + 32 * j];
-#pragma unroll
-  for (int i = 0; i < I4_MT; ++i) {
-    const float* sxr = xs + m0 + wm * 128 + i * 32 + 4 * lh;
-    float4 sx4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sx4[q] = *reinterpret_cast<const float4*>(sxr + 8 * q);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float4 q4 = sx4[v >> 2];
-        const float sxv = (v & 3) == 0 ? q4.x : (v & 3) == 1 ? q4.y : (v & 3) == 2 ? q4.z : q4.w;
-        out[i][j][v] = (float)acc[i][j][v] * (sxv * swc[j]);
-      }
-  }
-  if constexpr (NTR > 0) {
-#pragma unroll
-    for (int k0 = 0; k0 < RP; k0 += 32) {
-      v4i LB[KS][2];
-      float4 tv[KS][I4_MT][2];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int kk = k0 + 16 * s;
-        if (kk >= RP) break;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          LB[s][j] = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + bcol0 + j * 32) * RP + kk + 8 * lh);
-#pragma unroll
-        for (int i = 0; i < I4_MT; ++i) {
-          const int r = wm * 128 + i * 32 + lr;
-          const float* tp = T_LDS ? reinterpret_cast<const float*>(t_tile + r * TROWB) + kk + 8 * lh
-                                  : xl1 + (size_t)(m0 + r) * RP + kk + 8 * lh;
-          tv[s][i][0] = *reinterpret_cast<const float4*>(tp);
-          tv[s][i][1] = *reinterpret_cast<const float4*>(tp + 4);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (k0 + 16 * s >= RP) break;
-#pragma unroll
-        for (int i = 0; i < I4_MT; ++i) {
-          const float4 t0 = tv[s][i][0], t1 = tv[s][i][1];
-          const v4i TA = v4i{(int)pack_bf16x2(t0.x, t0.y), (int)pack_bf16x2(t0.z, t0.w), (int)pack_bf16x2(t1.x, t1.y),
-                             (int)pack_bf16x2(t1.z, t1.w)};
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            out[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(TA), as_bf16x8(LB[s][j]), out[i][j], 0, 0, 0);
-        }
-      }
-    }
-  }
-  uint8_t* stage = reinterpret_cast<uint8_t*>(ring[0]);
-#pragma unroll
-  for (int w = 1; w < I4_NS; ++w)
-    if (wave == w) stage = reinterpret_cast<uint8_t*>(ring[w]);  // wave-uniform select
-  static_assert(64 * Y_ES <= (int)sizeof(I8Slot), "staging fits a ring slot");
-  store_y(out, stage, bias, Y, ldy, M, N, m0 + wm * 128, n0 + wn * 64, lane);
-}
-
 // ----------------------------------------------------------------------------- launch helpers
 template <int FMT, int NT>
 hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, const uint16_t* l1t, int m_pad,
@@ -1010,10 +656,7 @@ hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (FMT == W4A4_FMT_W8A8) {  // per-token scales from the slices' partial maxima, then the codes
-    const int nkb = (K + Q8_KCHUNK - 1) / Q8_KCHUNK;
-    hipLaunchKernelGGL(quantize_w8_kernel, dim3(m_pad / Q8_ROWS * nkb), dim3(256), 0, st, X, M, K, ldx, il, m_pad, nsl,
-                       xq, static_cast<float*>(xs));
-    e = hipGetLastError();
+    e = launch_quantize_w8(X, M, K, ldx, il, m_pad, nsl, xq, static_cast<float*>(xs), st);
     if (e != hipSuccess) return e;
   }
   if (NT == 0 || nsl == 1) return hipSuccess;
@@ -1045,9 +688,6 @@ hipError_t launch_gemm(int fmt, const uint8_t* xq, const void* xs, const float* 
   if (fmt == W4A4_FMT_INT4_G64)
     hipLaunchKernelGGL((gemm_kernel<W4A4_FMT_INT4_G64, NTR>), grid, block, 0, st, xq, xsb, xl1, wq, wsb, l2t, bias, Y,
                        ldy, M, N, K, m_pad, n_pad);
-  else if (fmt == W4A4_FMT_W8A8)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<NTR>), grid, block, 0, st, xq, static_cast<const float*>(xs), xl1, wq,
-                       static_cast<const float*>(ws), l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
   else
     hipLaunchKernelGGL((gemm_kernel<W4A4_FMT_MXFP4_B32, NTR>), grid, block, 0, st, xq, xsb, xl1, wq, wsb, l2t, bias,
                        Y, ldy, M, N, K, m_pad, n_pad);
@@ -1105,8 +745,13 @@ w4a4_status_t w4a4_lowrank_linear(const uint8_t* xq, const void* xscale, const f
   if (rank > 0 && (!xl1 || !l2t || !aligned16(xl1) || !aligned16(l2t))) return W4A4_ERR_INVALID_ARG;
   if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return W4A4_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(Y) & 1u) return W4A4_ERR_INVALID_ARG;
-  hipError_t e = dispatch_gemm(rank_pad_of(rank) / 16, fmt, xq, xscale, xl1, wq, wscale, l2t, bias, Y, ldy, M, N, K,
-                               rows_pad_of(M), rows_pad_of(N), reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = fmt == W4A4_FMT_W8A8
+                     ? dispatch_gemm_w8a8(rank_pad_of(rank) / 16, xq, static_cast<const float*>(xscale), xl1, wq,
+                                          static_cast<const float*>(wscale), l2t, bias, Y, ldy, M, N, K,
+                                          rows_pad_of(M), rows_pad_of(N), hs)
+                     : dispatch_gemm(rank_pad_of(rank) / 16, fmt, xq, xscale, xl1, wq, wscale, l2t, bias, Y, ldy, M,
+                                     N, K, rows_pad_of(M), rows_pad_of(N), hs);
   return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP;
 }
 
