@@ -320,12 +320,16 @@ def main():
                            "unfused_lowrank_overhead_pct": round(100.0 * (msu - ms0) / ms0, 2)}
         del layer0, acts0, layer_u, acts_u, l1s, l2
         if fmt != "w8a8":
-            # the 8-bit setting (App. D: per-token / per-channel INT8) on the same layer and factors
-            prep8 = w4.prepare_weights(d["w"], lam, r, "w8a8", prep["l1"], prep["l2"])
+            # the 8-bit setting of App. D (per-token / per-channel INT8, rank 16) on the same layer:
+            # its rank-16 factors are the leading 16 of this layer's SVD factors
+            r8 = min(16, r)
+            prep8 = w4.prepare_weights(d["w"], lam, r8, "w8a8", prep["l1"][:, :r8], prep["l2"][:r8])
             layer8 = w4.W4A4Linear(prep8, inv, device=dev)
             ms8, g8 = time_layer(layer8, x, y, M, args.steps, args.warmup)
-            out["ablation"].update({"w8a8_ms_per_step": round(ms8, 5), "w8a8_gemm_avg_ms": round(g8, 5),
-                                    "w8a8_gemm_TOPS": round(ops / (g8 * 1e-3) / 1e12, 2),
+            ops8 = layer_ops(M, N, K, r8)
+            out["ablation"].update({"w8a8_rank": r8, "w8a8_ms_per_step": round(ms8, 5),
+                                    "w8a8_gemm_avg_ms": round(g8, 5),
+                                    "w8a8_gemm_TOPS": round(ops8 / (g8 * 1e-3) / 1e12, 2),
                                     "speedup_vs_w8a8": round(ms8 / ms_step, 3)})
             del layer8, prep8
     if args.copy_calibration:
