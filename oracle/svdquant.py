@@ -45,6 +45,11 @@ Readings of points the page leaves open (all listed in the design notes):
   2^e, e the smallest integer with 6·2^e >= max|v| (the power-of-two round-up of
   max|v|/qmax); element codes are E2M1 round-half-to-even of v / 2^e; the sign
   bit of v is kept even when the magnitude rounds to 0.
+* The MLP pair (fc1 → GELU → fc2) joined at the producer: fc2's activations are
+  X₂ = bf16(GELU(Y₁)) of fc1's bf16 output Y₁, with GELU(y) = y/2 · (1 + erf(y/√2))
+  evaluated in fp32 and erf taken from Abramowitz & Stegun 7.1.28 (a rational form
+  with |error| ≤ 3e-7, no exponential), so that a GPU kernel can take the same
+  fp32 steps and both sides round X₂ (and so decide fc2's codes) identically.
 """
 from __future__ import annotations
 
@@ -451,3 +456,45 @@ def prop41_terms(x: np.ndarray, w: np.ndarray, qx: np.ndarray, qw: np.ndarray):
     fro = np.linalg.norm
     bound = fro(x) * fro(w - qw) + fro(x - qx) * (fro(w) + fro(w - qw))
     return err, bound
+
+
+# ---------------------------------------------------------------- MLP producer: GELU → fc2 codes
+# Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.28:
+#   erf(x) ≈ 1 − (1 + a1 x + a2 x² + a3 x³ + a4 x⁴ + a5 x⁵ + a6 x⁶)^−16 for x ≥ 0, |ε| ≤ 3e−7.
+AS7128 = (0.0705230784, 0.0422820123, 0.0092705272, 0.0001520143, 0.0002765672, 0.0000430638)
+INV_SQRT2_F32 = np.float32(0.70710678118654752)
+
+
+def erf32(x) -> np.ndarray:
+    """erf in fp32 by A&S 7.1.28, one IEEE fp32 operation at a time: the polynomial by Horner's
+    rule from a6 down (multiply, then add), the 16th power by four squarings, 1 − 1/p¹⁶, and the
+    sign of x restored (erf is odd)."""
+    x = np.asarray(x, dtype=np.float32)
+    ax = np.abs(x)
+    f = np.float32
+    p = np.full_like(ax, f(AS7128[5]))
+    with np.errstate(over="ignore", divide="ignore"):  # p overflows to inf for large |x|: erf = ±1
+        for a in (AS7128[4], AS7128[3], AS7128[2], AS7128[1], AS7128[0], 1.0):
+            p = (p * ax).astype(np.float32)
+            p = (p + f(a)).astype(np.float32)
+        for _ in range(4):
+            p = (p * p).astype(np.float32)
+        e = (f(1.0) - (f(1.0) / p).astype(np.float32)).astype(np.float32)
+    return np.where(x < 0, -e, e).astype(np.float32)
+
+
+def gelu32(y) -> np.ndarray:
+    """GELU(y) = (y/2)·(1 + erf(y/√2)) in fp32: u = y·fp32(1/√2), e = erf32(u), (0.5·y)·(1 + e)."""
+    y = np.asarray(y, dtype=np.float32)
+    e = erf32((y * INV_SQRT2_F32).astype(np.float32))
+    return ((np.float32(0.5) * y).astype(np.float32) * (np.float32(1.0) + e).astype(np.float32)).astype(np.float32)
+
+
+def gelu_quantize(y1_bits: np.ndarray, inv_lam2: np.ndarray, l1_2: np.ndarray, fmt: str = FMT_INT4_G64):
+    """fc2's activation side computed from fc1's bf16 output Y₁ (bit patterns): X₂ = bf16(GELU(Y₁)),
+    then the ordinary activation side of fc2 (smoothing by 1/λ₂, codes and scales, t₂ = bf16(X̂₂)·L1₂).
+    Returns the activation dict plus ``x2_bits``."""
+    x2_bits = f32_to_bf16_bits(bf16_rne(gelu32(bf16_bits_to_f32(y1_bits))))
+    act = quantize_activations(x2_bits, inv_lam2, l1_2, fmt)
+    act["x2_bits"] = x2_bits
+    return act

@@ -486,3 +486,62 @@ def test_lora_merge_adds_exactly_the_lora_term():
     diff = (ym["y_m"] + ym["y_l"]) - (yb["y_m"] + yb["y_l"])
     assert np.allclose(diff, tb_a @ b.astype(np.float64), rtol=1e-12, atol=1e-15)
     assert np.array_equal(ym["cx"], yb["cx"]) and np.array_equal(ym["sx"], yb["sx"])
+
+
+# ---------------------------------------------------------------- MLP producer: fp32 GELU
+def _phi_gelu(y):
+    """Exact GELU in fp64 from math.erf (the textbook definition)."""
+    return 0.5 * y * (1.0 + math.erf(y / math.sqrt(2.0)))
+
+
+def test_erf32_within_the_rational_form_bound():
+    """A&S 7.1.28 is within 3e-7 of erf; fp32 evaluation (16th power by squaring) adds ≤ 1.5e-6."""
+    x = np.concatenate([np.linspace(-8, 8, 160001), [0.0, 1e-30, 1e-8, 3.0, 5.5, 40.0, 1e30]]).astype(np.float32)
+    e = O.erf32(x)
+    ref = np.array([math.erf(float(v)) for v in x])
+    assert np.abs(e - ref).max() <= 2e-6
+    assert np.array_equal(O.erf32(-x), -e)                     # odd, bit for bit
+    assert O.erf32(np.float32([0.0]))[0] == 0.0 and O.erf32(np.float32([40.0]))[0] == 1.0
+
+
+def test_gelu32_matches_the_erf_definition():
+    y = np.concatenate([np.linspace(-12, 12, 240001), [0.0, -0.0, 1e-20, 100.0, -100.0]]).astype(np.float32)
+    g = O.gelu32(y)
+    ref = np.array([_phi_gelu(float(v)) for v in y])
+    assert np.all(np.abs(g - ref) <= 1e-6 * np.maximum(1.0, np.abs(ref)))
+    assert O.gelu32(np.float32([100.0]))[0] == 100.0 and O.gelu32(np.float32([-100.0]))[0] == 0.0
+    assert O.gelu32(np.float32([0.0]))[0] == 0.0
+
+
+def test_gelu32_rounds_to_the_same_bf16_as_exact_gelu():
+    """Brute force over every bf16 value in [-16, 16]. Wherever |GELU(y)| >= 2^-6 (everything
+    but the far negative tail, where 1 + erf cancels and only the absolute bound holds),
+    bf16(gelu32(y)) is bf16 of the exact GELU unless the exact value lies within the fp32
+    evaluation error of a bf16 rounding midpoint; everywhere the bf16 results differ by at most
+    one bf16 step or 4e-6."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    y = O.bf16_bits_to_f32(bits)
+    y = y[np.isfinite(y) & (np.abs(y) <= 16)]
+    got = O.bf16_rne(O.gelu32(y)).astype(np.float64)
+    exact = np.array([_phi_gelu(float(v)) for v in y])
+    want = O.bf16_rne(exact).astype(np.float64)
+    big = np.abs(exact) >= 2.0 ** -6
+    differ = (got != want) & big
+    mid_dist = np.abs(np.abs(exact) - np.abs((got + want) / 2))
+    assert np.all(mid_dist[differ] <= 2e-6 * np.abs(exact[differ]))
+    assert differ.sum() <= 8
+    step = np.abs(want) * 2.0 ** -7
+    assert np.all(np.abs(got - want) <= np.maximum(step, 4e-6))
+
+
+def test_gelu_quantize_is_fc2_activation_side_of_gelu_output():
+    """fc2's codes from fc1's output are the ordinary activation side applied to X₂ = bf16(GELU(Y₁))."""
+    rng = np.random.default_rng(5)
+    y1 = O.f32_to_bf16_bits(O.bf16_rne(rng.standard_normal((20, 128)).astype(np.float32) * 3))
+    inv = (1.0 / rng.uniform(0.5, 2.0, 128)).astype(np.float32)
+    l1 = O.bf16_rne(rng.standard_normal((128, 8)).astype(np.float32) * 0.1)
+    act = O.gelu_quantize(y1, inv, l1)
+    x2 = O.bf16_rne(np.array([[_phi_gelu(float(v)) for v in row] for row in O.bf16_bits_to_f32(y1)]))
+    assert np.abs(O.bf16_bits_to_f32(act["x2_bits"]) - x2).max() <= 2.0 ** -8 * np.abs(x2).max()
+    direct = O.quantize_activations(act["x2_bits"], inv, l1)
+    assert np.array_equal(act["cx"], direct["cx"]) and np.array_equal(act["sx"], direct["sx"])
