@@ -217,6 +217,46 @@ w4a4_status_t w4a4_lowrank_linear(const uint8_t* xq, const void* xscale, const f
                                   const uint16_t* bias, uint16_t* Y, int ldy,
                                   int M, int N, int K, int rank, int fmt, w4a4_stream_t stream);
 
+/* ------------------------------------- the MLP pair, fc1 -> GELU -> fc2 (device, asynchronous) */
+
+/*
+ * GELU used between the two layers of the MLP (this library's fixed reading; the SVDQuant page
+ * names no formula): GELU(y) = (y/2)(1 + erf(y/sqrt 2)) in fp32 with erf from Abramowitz & Stegun
+ * 7.1.28, 1 - (1 + a1 x + ... + a6 x^6)^-16, |error| <= 3e-7, evaluated one IEEE fp32 operation at a
+ * time (Horner from a6, the 16th power by four squarings, correctly rounded division), so that
+ * the bf16 rounding of X2 = bf16(GELU(Y1)) is reproducible on a host.
+ *
+ * Consumer side: w4a4_quantize_act (INT4 only) applied to X = bf16(GELU(Y)) of a producer's bf16
+ * output Y [M][ldy] (device); every other argument as for w4a4_quantize_act.
+ */
+w4a4_status_t w4a4_gelu_quantize_act(const uint16_t* Y, int M, int K, int ldy, const float* inv_lambda,
+                                     const uint16_t* l1t, int rank, int fmt,
+                                     uint8_t* xq, void* xscale, float* xl1, w4a4_stream_t stream);
+
+/*
+ * Producer side (the quantizer fused into the producer's epilogue, §4.3's fusion principle one
+ * step upstream): the 4-bit GEMM of fc1 (arguments as for w4a4_lowrank_linear) whose epilogue
+ * emits fc2's activation side instead of fc1's output: X2 = bf16(GELU(bf16(Y1))) (padding rows:
+ * 0), smoothed by inv_lambda2 [N] (fc2's 1/lambda over fc2's K = this layer's N), quantized to
+ * fc2's INT4 codes xq2 [N/64][m_pad][32] and bf16 scales xscale2 [N/64][m_pad] (library layout,
+ * as w4a4_quantize_act writes them), and t2 = bf16(X2_hat)·L1_2 into xl1_2 ([m_pad][rank2_pad] fp32
+ * first, then per-256-column-tile partial planes as scratch; size from
+ * w4a4_gelu_quant_xl1_bytes). l1t2 is fc2's [rank2_pad][N] L1 transpose. Y [M][ldy] bf16 receives
+ * Y1 when not NULL (for checking; the fused path does not need it).
+ * Requires fmt == W4A4_FMT_INT4_G64, N a multiple of 64, rank <= 32 and rank2 <= 32
+ * (W4A4_ERR_UNSUPPORTED otherwise); xq2/xscale2/xl1_2 device buffers sized as w4a4_buffer_sizes
+ * gives them for fc2 (M rows, K = N), except xl1_2.
+ */
+w4a4_status_t w4a4_lowrank_linear_gelu_quant(const uint8_t* xq, const void* xscale, const float* xl1,
+                                             const uint8_t* wq, const void* wscale, const uint16_t* l2t,
+                                             const uint16_t* bias, int M, int N, int K, int rank, int fmt,
+                                             const float* inv_lambda2, const uint16_t* l1t2, int rank2,
+                                             uint8_t* xq2, void* xscale2, float* xl1_2, uint16_t* Y, int ldy,
+                                             w4a4_stream_t stream);
+
+/* Bytes of the xl1_2 buffer of w4a4_lowrank_linear_gelu_quant (0 when rank2 < 1 or M, N < 1). */
+size_t w4a4_gelu_quant_xl1_bytes(int M, int N, int rank2);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "w4a4.h")
 
 def test_library_exports_every_declared_symbol():
     decl = set(re.findall(r"\b(w4a4_[a-z0-9_]+)\s*\(", open(HEADER).read()))
-    assert len(decl) == 12, sorted(decl)
+    assert len(decl) == 15, sorted(decl)
     L = w4.lib()
     missing = [n for n in decl if not hasattr(L, n)]
     assert not missing, missing
@@ -304,3 +304,28 @@ def test_device_entry_points_validate_before_launch():
     assert L.w4a4_lowrank_linear(P(), P(), P(), P(), P(), None, None, P(), 16, 4, 16, 64, 8, 0, None) == 1
     assert L.w4a4_lowrank_linear(P(), P(), None, P(), P(), None, None, P(1), 16, 4, 16, 64, 0, 0, None) == 1
     assert L.w4a4_lowrank_linear(P(), P(), None, P(), P(), None, None, P(), 16, 4, 16, 64, 0, 9, None) == 2
+
+
+def test_mlp_pair_entry_points_validate_before_launch():
+    """The GELU paths accept INT4 only, ranks <= 32 for the fused GEMM, and whole 64-groups."""
+    L = w4.lib()
+    al = np.zeros(1 << 12, np.uint8)
+    base = al.ctypes.data + (-al.ctypes.data) % 256
+    P = lambda off=0: ctypes.c_void_p(base + off)
+    assert L.w4a4_gelu_quantize_act(P(), 4, 64, 64, P(), None, 0, 1, P(), P(), None, None) == 2   # MXFP4
+    assert L.w4a4_gelu_quantize_act(P(), 4, 64, 32, P(), None, 0, 0, P(), P(), None, None) == 1   # ldy < K
+    assert L.w4a4_gelu_quantize_act(None, 4, 64, 64, P(), None, 0, 0, P(), P(), None, None) == 1
+    args = lambda **kw: dict(dict(xq=P(), xs=P(), xl1=None, wq=P(), ws=P(), l2t=None, bias=None, M=4, N=128, K=64,
+                                  rank=0, fmt=0, il2=P(), l1t2=None, rank2=0, xq2=P(), xs2=P(), xl12=None, Y=None,
+                                  ldy=0), **kw)
+    call = lambda a: L.w4a4_lowrank_linear_gelu_quant(*a.values(), None)
+    assert call(args(fmt=1)) == 2
+    assert call(args(rank=33, N=256, K=64, xl1=P(), l2t=P())) in (1, 2)
+    assert call(args(rank2=33, l1t2=P(), xl12=P())) == 2
+    assert call(args(N=96)) == 1                     # fc2's K = N must be whole 64-groups
+    assert call(args(il2=None)) == 1
+    assert call(args(rank2=8)) == 1                  # rank2 without L1_2 / t2 buffers
+    assert call(args(Y=P(1), ldy=128)) == 1          # misaligned Y
+    assert w4.gelu_quant_xl1_bytes(300, 640, 20) == 512 * 32 * 4 * (1 + 3)
+    assert w4.gelu_quant_xl1_bytes(300, 256, 20) == 512 * 32 * 4
+    assert w4.gelu_quant_xl1_bytes(300, 256, 0) == 0

@@ -22,6 +22,7 @@ __all__ = [
     "FMT_INT4_G64", "FMT_MXFP4_B32", "GROUP", "ROW_ALIGN", "MAX_RANK", "W4A4Error", "lib", "lib_path",
     "buffer_sizes", "column_absmax", "smooth_factors", "prepare_weights", "append_lowrank",
     "codes_to_canonical", "scales_to_canonical", "quantize_act", "lowrank_linear", "W4A4Linear",
+    "FMT_W8A8", "gelu_quantize_act", "lowrank_linear_gelu_quant", "gelu_quant_xl1_bytes", "MLPPair",
 ]
 
 FMT_INT4_G64 = 0
@@ -81,12 +82,15 @@ def lib() -> ctypes.CDLL:
             "w4a4_scales_to_canonical": [P, I, I, I, P],
             "w4a4_quantize_act": [P, I, I, I, P, P, I, I, P, P, P, P],
             "w4a4_lowrank_linear": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P],
+            "w4a4_gelu_quantize_act": [P, I, I, I, P, P, I, I, P, P, P, P],
+            "w4a4_lowrank_linear_gelu_quant": [P, P, P, P, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, I, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = I
-        _ = S
+        L.w4a4_gelu_quant_xl1_bytes.argtypes = [I, I, I]
+        L.w4a4_gelu_quant_xl1_bytes.restype = S
         _lib = L
     return _lib
 
@@ -243,6 +247,28 @@ def lowrank_linear(xq, xscale, xl1, wq, wscale, l2t, bias, y, M, N, K, rank, fmt
         y.stride(0), M, N, K, rank, _fmt(fmt), _stream(stream)))
 
 
+def gelu_quantize_act(y, inv_lambda, l1t, rank, fmt, xq, xscale, xl1, stream=None):
+    """The activation kernel on X = bf16(GELU(y)) of a producer's bf16 output y [M, K] (INT4)."""
+    M, K = y.shape
+    _check("w4a4_gelu_quantize_act", lib().w4a4_gelu_quantize_act(
+        _dptr(y), M, K, y.stride(0), _dptr(inv_lambda), _dptr(l1t), rank, _fmt(fmt), _dptr(xq), _dptr(xscale),
+        _dptr(xl1), _stream(stream)))
+
+
+def lowrank_linear_gelu_quant(xq, xscale, xl1, wq, wscale, l2t, bias, M, N, K, rank, fmt, inv_lambda2, l1t2, rank2,
+                              xq2, xscale2, xl1_2, y=None, stream=None):
+    """fc1's GEMM with fc2's activation side (GELU, smoothing, INT4 codes, t2) in its epilogue;
+    y (optional, [M, >=N] bf16) receives fc1's output for checking."""
+    _check("w4a4_lowrank_linear_gelu_quant", lib().w4a4_lowrank_linear_gelu_quant(
+        _dptr(xq), _dptr(xscale), _dptr(xl1), _dptr(wq), _dptr(wscale), _dptr(l2t), _dptr(bias), M, N, K, rank,
+        _fmt(fmt), _dptr(inv_lambda2), _dptr(l1t2), rank2, _dptr(xq2), _dptr(xscale2), _dptr(xl1_2), _dptr(y),
+        0 if y is None else y.stride(0), _stream(stream)))
+
+
+def gelu_quant_xl1_bytes(M: int, N: int, rank2: int) -> int:
+    return int(lib().w4a4_gelu_quant_xl1_bytes(M, N, rank2))
+
+
 class W4A4Linear:
     """A prepared layer resident in HBM: codes, scales and low-rank factors of one weight.
 
@@ -293,3 +319,48 @@ class W4A4Linear:
             y = torch.empty((M, self.N), dtype=torch.bfloat16, device=self.device)
         a = self.quantize(x, stream)
         return self.gemm(a, M, y, stream)
+
+
+class MLPPair:
+    """fc1 -> GELU -> fc2, both prepared W4A4 layers resident in HBM (fc2's K = fc1's N).
+
+    ``fused(x)``: fc1's activation kernel, then fc1's GEMM with fc2's activation side in its
+    epilogue (no fc1 output in HBM), then fc2's GEMM. ``unfused(x)``: fc1's two kernels writing
+    Y1, fc2's activation kernel applying the GELU to Y1 as it reads it, fc2's GEMM."""
+
+    def __init__(self, fc1: W4A4Linear, fc2: W4A4Linear):
+        assert fc2.K == fc1.N, "fc2's K must be fc1's N"
+        self.fc1, self.fc2 = fc1, fc2
+        self._buf = {}
+
+    def buffers(self, M: int):
+        import torch
+        if M not in self._buf:
+            dev = self.fc1.device
+            b = dict(y1=torch.empty((M, self.fc1.N), dtype=torch.bfloat16, device=dev))
+            b["act2"] = self.fc2.act_buffers(M)
+            n = gelu_quant_xl1_bytes(M, self.fc1.N, self.fc2.rank) // 4
+            b["xl1_2_fused"] = torch.empty(max(n, 16), dtype=torch.float32, device=dev) if self.fc2.rank else None
+            self._buf[M] = b
+        return self._buf[M]
+
+    def fused(self, x, y2, y1_check=None, stream=None):
+        M = x.shape[0]
+        b = self.buffers(M)
+        a1 = self.fc1.quantize(x, stream)
+        f1, f2, a2 = self.fc1, self.fc2, b["act2"]
+        lowrank_linear_gelu_quant(a1["xq"], a1["xscale"], a1["xl1"], f1.wq, f1.wscale, f1.l2t, f1.bias, M, f1.N, f1.K,
+                                  f1.rank, f1.fmt, f2.inv_lambda, f2.l1t, f2.rank, a2["xq"], a2["xscale"],
+                                  b["xl1_2_fused"], y1_check, stream)
+        a2f = dict(a2, xl1=b["xl1_2_fused"])
+        f2.gemm(a2f, M, y2, stream)
+        return a2f
+
+    def unfused(self, x, y2, stream=None):
+        M = x.shape[0]
+        b = self.buffers(M)
+        self.fc1(x, b["y1"], stream)
+        f2, a2 = self.fc2, b["act2"]
+        gelu_quantize_act(b["y1"], f2.inv_lambda, f2.l1t, f2.rank, f2.fmt, a2["xq"], a2["xscale"], a2["xl1"], stream)
+        f2.gemm(a2, M, y2, stream)
+        return a2

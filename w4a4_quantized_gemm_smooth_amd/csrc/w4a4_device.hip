@@ -46,6 +46,60 @@ __device__ __forceinline__ v8i unfold_fp6(v4i d) {
              d[2] & (int)FOLD_C0, (d[2] & (int)FOLD_C34) | (d[3] & (int)FOLD_C05), d[3] & (int)FOLD_C2, 0, 0};
 }
 
+// GELU(y) = (y/2)·(1 + erf(y/√2)) in fp32, erf from Abramowitz & Stegun 7.1.28
+// (1 − (1 + a1 x + … + a6 x⁶)^−16, |error| ≤ 3e−7), one IEEE operation at a time (this file is built
+// with -ffp-contract=off; the division is correctly rounded), so the bf16 rounding of the result
+// is reproducible by any host that takes the same steps. Constants are the fp32 roundings of the
+// published coefficients and of 1/√2.
+__device__ __forceinline__ float gelu32(float y) {
+  const float u = y * 0x1.6a09e6p-1f;
+  const float ax = fabsf(u);
+  float p = 0x1.693ecep-15f;  // a6
+  p = p * ax + 0x1.220072p-12f;
+  p = p * ax + 0x1.3ecc0ep-13f;
+  p = p * ax + 0x1.2fc6d2p-7f;
+  p = p * ax + 0x1.5a5fcep-5f;
+  p = p * ax + 0x1.20dccep-4f;  // a1
+  p = p * ax + 1.0f;
+  p = p * p;
+  p = p * p;
+  p = p * p;
+  p = p * p;
+  float e = 1.0f - 1.0f / p;
+  e = u < 0.f ? -e : e;
+  return (0.5f * y) * (1.0f + e);
+}
+
+// INT4 codes of one group row held by four lanes (lane bits 4-5 = kc, 16 values each): s =
+// bf16(max|X̂| / 7) (0 below 2^-126), q = rint(X̂ · (1/s)) (|q| <= 7 by the symmetric scale). The fp32
+// product is formed as in the method, and v_cvt_scalef32_2xpk16_fp6_f32 rounds y / 8 to
+// nearest-even on the E2M3 subnormal grid (step 1/8), i.e. emits exactly the carrier field
+// sign|00|rint(y). Its two sources interleave (field 2e = src0[e], field 2e+1 = src1[e]); fields
+// 16..31 are unused. Returns the lane's 16 codes folded into 8 bytes and the scale's bf16 bits.
+__device__ __forceinline__ uint2 quant_int4_lane(const float (&xh)[2][8], uint32_t& s_bits) {
+  float amax = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xh[h][e]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  float s = bf16f(bf16_rne(amax / 7.0f));
+  if (!(s >= 0x1p-126f)) s = 0.f;
+  const float inv = s != 0.f ? 1.0f / s : 0.f;
+  v16f ev, od;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ev[e] = xh[e >> 2][2 * (e & 3)] * inv;
+    od[e] = xh[e >> 2][2 * (e & 3) + 1] * inv;
+    ev[8 + e] = 0.f;
+    od[8 + e] = 0.f;
+  }
+  const v6i img = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
+  s_bits = bf16_rne(s);
+  return fold_fp6((uint32_t)img[0], (uint32_t)img[1], (uint32_t)img[2]);
+}
+
 // ===================================================================================
 // Kernel 1: activation side. Per row and group: X̂ = fp32(x * inv_lambda); codes + scales;
 // t += bf16(X̂) · L1 (MFMA). One block = 128 rows (8 waves of 16) x one slice of at most
@@ -61,7 +115,9 @@ constexpr int QA_WAVES = QA_BLOCK_ROWS / 16;
 // whole 64-slot DMA instructions
 constexpr int qa_lds_slots(int rp, int gs) { return (gs * 16 + rp * (gs * 8 + 1) + 63) / 64 * 64; }
 
-template <int FMT, int NT>  // NT = rank_pad / 16 (0 when there is no low-rank branch)
+// GELU_IN: the input is a producer's bf16 output Y and the layer's activations are
+// X = bf16(GELU(Y)) (the MLP's fc2; INT4 only)
+template <int FMT, int NT, bool GELU_IN = false>  // NT = rank_pad / 16 (0 when there is no low-rank branch)
 __global__ __launch_bounds__(QA_WAVES * 64, NT <= 2 ? 4 : 2) void quantize_act_kernel(
     // X is not restrict: its loads must stay ahead of the counted wait below
     const uint16_t* X, int M, int K, int ldx, const float* __restrict__ inv_lambda,
@@ -133,7 +189,8 @@ __global__ __launch_bounds__(QA_WAVES * 64, NT <= 2 ? 4 : 2) void quantize_act_k
       const float ilv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (e & 1) ? (xw[e >> 1] >> 16) : (xw[e >> 1] & 0xFFFFu);
+        uint32_t bits = (e & 1) ? (xw[e >> 1] >> 16) : (xw[e >> 1] & 0xFFFFu);
+        if (GELU_IN) bits = bf16_rne(gelu32(bf16f(bits)));
         xh[h][e] = bf16f(bits) * ilv[e];  // one fp32 multiply (no contraction: nothing to fuse)
       }
     }
@@ -144,31 +201,9 @@ __global__ __launch_bounds__(QA_WAVES * 64, NT <= 2 ? 4 : 2) void quantize_act_k
 #pragma unroll
         for (int e = 0; e < 8; ++e) row_amax = fmaxf(row_amax, fabsf(xh[h][e]));
     } else if constexpr (FMT == W4A4_FMT_INT4_G64) {
-      float amax = 0.f;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xh[h][e]));
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      float s = bf16f(bf16_rne(amax / 7.0f));
-      if (!(s >= 0x1p-126f)) s = 0.f;
-      const float inv = s != 0.f ? 1.0f / s : 0.f;
-      // q = rint(X̂ * (1/s)) (|q| <= 7 by the symmetric scale): the fp32 product is formed as in
-      // the method, and v_cvt_scalef32_2xpk16_fp6_f32 rounds y / 8 to nearest-even on the E2M3
-      // subnormal grid (step 1/8), i.e. emits exactly the carrier field sign|00|rint(y). Its two
-      // sources interleave (field 2e = src0[e], field 2e+1 = src1[e]); fields 16..31 are unused.
-      v16f ev, od;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ev[e] = xh[e >> 2][2 * (e & 3)] * inv;
-        od[e] = xh[e >> 2][2 * (e & 3) + 1] * inv;
-        ev[8 + e] = 0.f;
-        od[8 + e] = 0.f;
-      }
-      const v6i img = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
-      *qdst = fold_fp6((uint32_t)img[0], (uint32_t)img[1], (uint32_t)img[2]);
-      if (kc == 0) static_cast<uint16_t*>(xscale)[(size_t)g * m_pad + row] = (uint16_t)bf16_rne(s);
+      uint32_t sb;
+      *qdst = quant_int4_lane(xh, sb);
+      if (kc == 0) static_cast<uint16_t*>(xscale)[(size_t)g * m_pad + row] = (uint16_t)sb;
     } else {
       // the lane's 16 values lie in 32-block kc / 2, shared with lane kc ^ 1
       float amax = 0.f;
@@ -286,12 +321,37 @@ struct I4Slot {
   uint16_t z[32];  // zeros (never written by the DMA): k > 0 half of the scale outer-product operand
 };
 
-template <int FMT, int NTR>  // NTR = rank_pad / 16
+// The next layer's activation side in this GEMM's epilogue (the MLP's fc1 -> GELU -> fc2 join):
+// fc2's 1/λ over this layer's N columns, fc2's L1ᵀ [rank2_pad][N], and fc2's outputs in library
+// layout: INT4 codes [N/64][m_pad][32 B], bf16 scales [N/64][m_pad], and one partial t plane
+// [m_pad][rank2_pad] per 256-column tile of this layer.
+struct GeluQuantArgs {
+  const float* il2;
+  const uint16_t* l1t2;
+  uint8_t* xq2;
+  uint16_t* xs2;
+  float* t2part;
+};
+
+// the block's eight ring slots, by value (indexed with constants only, so they stay in registers)
+struct SlotSet {
+  uint8_t* s[I4_NS];
+};
+
+template <int NT2>
+__device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8_t* stage, SlotSet slots,
+                                                    const GeluQuantArgs& fa, const uint16_t* bias, int M, int N,
+                                                    int m_pad, int m0, int n0, int tn, int wm, int wn, int wave,
+                                                    int lane);
+
+// FUSE < 0: the plain GEMM (fa unused). FUSE >= 0 (INT4 only): fc1 of the MLP with fc2's
+// activation side in the epilogue, FUSE = fc2's rank_pad / 16; Y may then be NULL.
+template <int FMT, int NTR, int FUSE = -1>  // NTR = rank_pad / 16
 __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ xl1,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
-    int m_pad, int n_pad) {
+    int m_pad, int n_pad, GeluQuantArgs fa) {
   constexpr bool INT4 = FMT == W4A4_FMT_INT4_G64;
   __shared__ __attribute__((aligned(16))) I4Slot sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7;
   I4Slot* const ring[I4_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5, &sl6, &sl7};
@@ -637,21 +697,158 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   for (int w = 1; w < I4_NS; ++w)
     if (wave == w) stage = reinterpret_cast<uint8_t*>(ring[w]);  // wave-uniform select
   static_assert(64 * Y_ES <= (int)sizeof(I4Slot), "staging fits a ring slot");
-  store_y(acc, stage, bias, Y, ldy, M, N, m0 + wm * 128, n0 + wn * 64, lane);
+  if constexpr (FUSE < 0) {
+    store_y(acc, stage, bias, Y, ldy, M, N, m0 + wm * 128, n0 + wn * 64, lane);
+  } else {
+    if (Y) store_y(acc, stage, bias, Y, ldy, M, N, m0 + wm * 128, n0 + wn * 64, lane);  // for checking
+    const SlotSet slots{{reinterpret_cast<uint8_t*>(&sl0), reinterpret_cast<uint8_t*>(&sl1),
+                         reinterpret_cast<uint8_t*>(&sl2), reinterpret_cast<uint8_t*>(&sl3),
+                         reinterpret_cast<uint8_t*>(&sl4), reinterpret_cast<uint8_t*>(&sl5),
+                         reinterpret_cast<uint8_t*>(&sl6), reinterpret_cast<uint8_t*>(&sl7)}};
+    gelu_quant_epilogue<FUSE>(acc, stage, slots, fa, bias, M, N, m_pad, m0, n0, tn, wm, wn, wave, lane);
+  }
+}
+
+
+// fc2's activation side from this wave's 128 x 64 block of fc1 results: X₂ = bf16(GELU(bf16(acc +
+// bias))) (padding rows: 0), staged in the wave's ring slot 64 rows at a time (row stride Y_ES),
+// read back with the activation kernel's lane layout (16 rows x 4 lanes of 16 values per pass),
+// smoothed, quantized to INT4 codes of fc2's group n0/64 + wn, and multiplied into partial
+// t₂ = bf16(X̂₂)·L1₂ (16x16x32 bf16 MFMAs, L1₂ operands loaded once). The four waves that share
+// block rows then sum their partials through LDS in a fixed order into this tile's plane.
+template <int NT2>
+__device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8_t* stage, SlotSet slots,
+                                                    const GeluQuantArgs& fa, const uint16_t* bias, int M, int N,
+                                                    int m_pad, int m0, int n0, int tn, int wm, int wn, int wave,
+                                                    int lane) {
+  constexpr int RP2 = NT2 * 16, NT2A = NT2 > 0 ? NT2 : 1;
+  const int lr = lane & 31, lh = lane >> 5;  // 32x32 MFMA output layout
+  const int r = lane & 15, kc = lane >> 4;   // activation-kernel layout
+  const int gcol0 = n0 + wn * 64;
+  const bool gvalid = gcol0 < N;  // N is a multiple of 64: the wave's columns are one whole group
+  const int g2 = gcol0 >> 6;
+  float bcol[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = gcol0 + j * 32 + lr;
+    bcol[j] = (bias && col < N) ? bf16f(bias[col]) : 0.f;
+  }
+  float il[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = gvalid ? *reinterpret_cast<const float4*>(fa.il2 + gcol0 + kc * 16 + 4 * q) : float4{0.f, 0.f, 0.f, 0.f};
+    il[4 * q] = v.x;
+    il[4 * q + 1] = v.y;
+    il[4 * q + 2] = v.z;
+    il[4 * q + 3] = v.w;
+  }
+  v4i B2[NT2A][2];
+  v4f tacc[8][NT2A];
+#pragma unroll
+  for (int c = 0; c < NT2A; ++c) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      B2[c][h] = (NT2 > 0 && gvalid)
+                     ? *reinterpret_cast<const v4i*>(fa.l1t2 + (size_t)(c * 16 + r) * N + gcol0 + kc * 16 + 8 * h)
+                     : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < 8; ++p) tacc[p][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const int rl = ii * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+          const int grow = m0 + wm * 128 + half * 64 + rl;  // rows grow, grow + 1
+          const uint32_t y = pack_bf16x2(acc[2 * half + ii][j][v] + bcol[j], acc[2 * half + ii][j][v + 1] + bcol[j]);
+          const uint32_t x0 = grow < M ? bf16_rne(gelu32(bf16f(y & 0xFFFFu))) : 0u;
+          const uint32_t x1 = grow + 1 < M ? bf16_rne(gelu32(bf16f(y >> 16))) : 0u;
+          uint16_t* d = reinterpret_cast<uint16_t*>(stage + rl * Y_ES + (j * 32 + lr) * 2);
+          d[0] = (uint16_t)x0;
+          d[Y_ES / 2] = (uint16_t)x1;
+        }
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int rr = pass * 16 + r;
+      const int row = m0 + wm * 128 + half * 64 + rr;
+      const uint4 lo = *reinterpret_cast<const uint4*>(stage + rr * Y_ES + kc * 32);
+      const uint4 hi = *reinterpret_cast<const uint4*>(stage + rr * Y_ES + kc * 32 + 16);
+      const uint32_t xw[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      float xh[2][8];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t bits = (e & 1) ? (xw[e >> 1] >> 16) : (xw[e >> 1] & 0xFFFFu);
+        xh[e >> 3][e & 7] = bf16f(bits) * il[e];  // X̂₂, one fp32 multiply
+      }
+      uint32_t sb;
+      const uint2 q = quant_int4_lane(xh, sb);
+      if (gvalid) {
+        *reinterpret_cast<uint2*>(fa.xq2 + ((size_t)g2 * m_pad + row) * 32 + kc * 8) = q;
+        if (kc == 0) fa.xs2[(size_t)g2 * m_pad + row] = (uint16_t)sb;
+      }
+      if constexpr (NT2 > 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          v4i a;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) a[d] = (int)pack_bf16x2(xh[h][2 * d], xh[h][2 * d + 1]);
+#pragma unroll
+          for (int c = 0; c < NT2; ++c)
+            tacc[half * 4 + pass][c] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(B2[c][h]), tacc[half * 4 + pass][c], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if constexpr (NT2 > 0) {
+    // 16x16 MFMA output: lane holds rank column c*16 + lane%16, rows 4*(lane/16) + v of its pass
+    __builtin_amdgcn_s_barrier();  // every wave is done with its staging slot
+    float* mine = reinterpret_cast<float*>(stage);  // the wave's own slot
+    static_assert(128 * RP2 * 4 <= (int)sizeof(I4Slot), "a wave's partial t fits its ring slot");
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+#pragma unroll
+      for (int c = 0; c < NT2; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mine[(p * 16 + 4 * kc + v) * RP2 + c * 16 + r] = tacc[p][c][v];
+    __builtin_amdgcn_s_barrier();
+    const int tid = wave * 64 + lane;
+    constexpr int Q = RP2 / 4;  // float4 per row
+#pragma unroll
+    for (int idx0 = 0; idx0 < 256 * Q; idx0 += I4_THREADS) {
+      const int idx = idx0 + tid, row = idx / Q, q = idx % Q;
+      const int wr = row >> 7, lrow = row & 127;
+      float4 sum = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {  // the four column waves of these rows, in order
+        const float* src = reinterpret_cast<const float*>(wr ? slots.s[4 + w] : slots.s[w]);
+        const float4 v = *reinterpret_cast<const float4*>(src + lrow * RP2 + 4 * q);
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+      }
+      *reinterpret_cast<float4*>(fa.t2part + ((size_t)tn * m_pad + m0 + row) * RP2 + 4 * q) = sum;
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------- launch helpers
-template <int FMT, int NT>
+template <int FMT, int NT, bool GELU_IN = false>
 hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, const uint16_t* l1t, int m_pad,
                      uint8_t* xq, void* xs, float* xl1, hipStream_t st) {
   const int gs = qa_group_slice(M, K), nsl = qa_slices(M, K);
   const size_t lds = 16 * (size_t)qa_lds_slots(NT * 16, gs);
   if (lds > 65536) {  // large ranks: allow the block more than 64 KB of dynamic LDS
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&quantize_act_kernel<FMT, NT>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&quantize_act_kernel<FMT, NT, GELU_IN>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
   }
-  hipLaunchKernelGGL((quantize_act_kernel<FMT, NT>), dim3(m_pad / QA_BLOCK_ROWS * nsl), dim3(QA_WAVES * 64), lds, st,
+  hipLaunchKernelGGL((quantize_act_kernel<FMT, NT, GELU_IN>), dim3(m_pad / QA_BLOCK_ROWS * nsl), dim3(QA_WAVES * 64), lds, st,
                      X, M, K, ldx, il, l1t, m_pad, gs, xq, xs, xl1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -665,12 +862,12 @@ hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, 
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, bool GELU_IN = false>
 hipError_t dispatch_qa(int nt, const uint16_t* X, int M, int K, int ldx, const float* il, const uint16_t* l1t,
                        int m_pad, uint8_t* xq, void* xs, float* xl1, hipStream_t st) {
   switch (nt) {
 #define W4A4_QA_CASE(n) \
-  case n: return launch_qa<FMT, n>(X, M, K, ldx, il, l1t, m_pad, xq, xs, xl1, st);
+  case n: return launch_qa<FMT, n, GELU_IN>(X, M, K, ldx, il, l1t, m_pad, xq, xs, xl1, st);
     W4A4_QA_CASE(0) W4A4_QA_CASE(1) W4A4_QA_CASE(2) W4A4_QA_CASE(3) W4A4_QA_CASE(4)
     W4A4_QA_CASE(5) W4A4_QA_CASE(6) W4A4_QA_CASE(7) W4A4_QA_CASE(8)
 #undef W4A4_QA_CASE
@@ -687,11 +884,41 @@ hipError_t launch_gemm(int fmt, const uint8_t* xq, const void* xs, const float* 
   const uint8_t* wsb = static_cast<const uint8_t*>(ws);
   if (fmt == W4A4_FMT_INT4_G64)
     hipLaunchKernelGGL((gemm_kernel<W4A4_FMT_INT4_G64, NTR>), grid, block, 0, st, xq, xsb, xl1, wq, wsb, l2t, bias, Y,
-                       ldy, M, N, K, m_pad, n_pad);
+                       ldy, M, N, K, m_pad, n_pad, GeluQuantArgs{});
   else
     hipLaunchKernelGGL((gemm_kernel<W4A4_FMT_MXFP4_B32, NTR>), grid, block, 0, st, xq, xsb, xl1, wq, wsb, l2t, bias,
-                       Y, ldy, M, N, K, m_pad, n_pad);
+                       Y, ldy, M, N, K, m_pad, n_pad, GeluQuantArgs{});
   return hipGetLastError();
+}
+
+template <int NTR, int NT2>
+hipError_t launch_gemm_gelu_quant(const uint8_t* xq, const void* xs, const float* xl1, const uint8_t* wq,
+                                  const void* ws, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy,
+                                  int M, int N, int K, int m_pad, int n_pad, const GeluQuantArgs& fa, float* t2,
+                                  hipStream_t st) {
+  const int tiles_n = n_pad / I4_BN;
+  hipLaunchKernelGGL((gemm_kernel<W4A4_FMT_INT4_G64, NTR, NT2>), dim3((m_pad / I4_BM) * tiles_n), dim3(I4_THREADS), 0, st, xq,
+                     static_cast<const uint8_t*>(xs), xl1, wq, static_cast<const uint8_t*>(ws), l2t, bias, Y, ldy, M, N,
+                     K, m_pad, n_pad, fa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || NT2 == 0 || tiles_n == 1) return e;
+  const int n = m_pad * NT2 * 16;
+  hipLaunchKernelGGL(t_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, fa.t2part, tiles_n, n, t2);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_gemm_gelu_quant(int ntr, int nt2, const uint8_t* xq, const void* xs, const float* xl1,
+                                    const uint8_t* wq, const void* ws, const uint16_t* l2t, const uint16_t* bias,
+                                    uint16_t* Y, int ldy, int M, int N, int K, int m_pad, int n_pad,
+                                    const GeluQuantArgs& fa, float* t2, hipStream_t st) {
+#define W4A4_GQ_CASE(a, b)                                                                                      \
+  if (ntr == a && nt2 == b)                                                                                      \
+    return launch_gemm_gelu_quant<a, b>(xq, xs, xl1, wq, ws, l2t, bias, Y, ldy, M, N, K, m_pad, n_pad, fa, t2, st);
+  W4A4_GQ_CASE(0, 0) W4A4_GQ_CASE(0, 1) W4A4_GQ_CASE(0, 2)
+  W4A4_GQ_CASE(1, 0) W4A4_GQ_CASE(1, 1) W4A4_GQ_CASE(1, 2)
+  W4A4_GQ_CASE(2, 0) W4A4_GQ_CASE(2, 1) W4A4_GQ_CASE(2, 2)
+#undef W4A4_GQ_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t dispatch_gemm(int ntr, int fmt, const uint8_t* xq, const void* xs, const float* xl1, const uint8_t* wq,
@@ -753,6 +980,59 @@ w4a4_status_t w4a4_lowrank_linear(const uint8_t* xq, const void* xscale, const f
                      : dispatch_gemm(rank_pad_of(rank) / 16, fmt, xq, xscale, xl1, wq, wscale, l2t, bias, Y, ldy, M,
                                      N, K, rows_pad_of(M), rows_pad_of(N), hs);
   return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP;
+}
+
+w4a4_status_t w4a4_gelu_quantize_act(const uint16_t* Y, int M, int K, int ldy, const float* inv_lambda,
+                                     const uint16_t* l1t, int rank, int fmt, uint8_t* xq, void* xscale, float* xl1,
+                                     w4a4_stream_t stream) {
+  if (!fmt_known(fmt)) return W4A4_ERR_UNSUPPORTED;
+  if (fmt != W4A4_FMT_INT4_G64) return W4A4_ERR_UNSUPPORTED;
+  w4a4_status_t st = check_shape(M, rank > 0 ? rank : 1, K, rank, fmt);
+  if (st != W4A4_OK) return st;
+  if (!Y || !inv_lambda || !xq || !xscale) return W4A4_ERR_INVALID_ARG;
+  if (ldy < K || ldy % 8 != 0) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(Y) || !aligned16(inv_lambda) || !aligned16(xq) || !aligned16(xscale)) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!l1t || !xl1 || !aligned16(l1t) || !aligned16(xl1))) return W4A4_ERR_INVALID_ARG;
+  const hipError_t e = dispatch_qa<W4A4_FMT_INT4_G64, true>(rank_pad_of(rank) / 16, Y, M, K, ldy, inv_lambda, l1t,
+                                                            rows_pad_of(M), xq, xscale, xl1,
+                                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP;
+}
+
+w4a4_status_t w4a4_lowrank_linear_gelu_quant(const uint8_t* xq, const void* xscale, const float* xl1,
+                                             const uint8_t* wq, const void* wscale, const uint16_t* l2t,
+                                             const uint16_t* bias, int M, int N, int K, int rank, int fmt,
+                                             const float* inv_lambda2, const uint16_t* l1t2, int rank2,
+                                             uint8_t* xq2, void* xscale2, float* xl1_2, uint16_t* Y, int ldy,
+                                             w4a4_stream_t stream) {
+  w4a4_status_t st = check_shape(M, N, K, rank, fmt);
+  if (st != W4A4_OK) return st;
+  if (fmt != W4A4_FMT_INT4_G64 || rank > 32 || rank2 > 32) return W4A4_ERR_UNSUPPORTED;
+  // the next layer's K is this layer's N: whole groups of 64
+  st = check_shape(M, rank2 > 0 ? rank2 : 1, N, rank2, fmt);
+  if (st != W4A4_OK) return st;
+  if (!xq || !xscale || !wq || !wscale || !inv_lambda2 || !xq2 || !xscale2) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(xscale) || !aligned16(wq) || !aligned16(wscale)) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(inv_lambda2) || !aligned16(xq2) || !aligned16(xscale2)) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!xl1 || !l2t || !aligned16(xl1) || !aligned16(l2t))) return W4A4_ERR_INVALID_ARG;
+  if (rank2 > 0 && (!l1t2 || !xl1_2 || !aligned16(l1t2) || !aligned16(xl1_2))) return W4A4_ERR_INVALID_ARG;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return W4A4_ERR_INVALID_ARG;
+  if (Y && ((reinterpret_cast<uintptr_t>(Y) & 1u) || ldy < N)) return W4A4_ERR_INVALID_ARG;
+  const int m_pad = rows_pad_of(M), n_pad = rows_pad_of(N), rp2 = rank_pad_of(rank2);
+  const int tiles_n = n_pad / 256;
+  GeluQuantArgs fa{inv_lambda2, l1t2, xq2, static_cast<uint16_t*>(xscale2),
+                   rank2 > 0 ? (tiles_n > 1 ? xl1_2 + (size_t)m_pad * rp2 : xl1_2) : nullptr};
+  const hipError_t e = dispatch_gemm_gelu_quant(rank_pad_of(rank) / 16, rp2 / 16, xq, xscale, xl1, wq, wscale, l2t,
+                                                bias, Y, ldy, M, N, K, m_pad, n_pad, fa, xl1_2,
+                                                reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP;
+}
+
+size_t w4a4_gelu_quant_xl1_bytes(int M, int N, int rank2) {
+  if (M < 1 || N < 1 || rank2 < 1) return 0;
+  const size_t t = size_t(rows_pad_of(M)) * size_t(rank_pad_of(rank2)) * 4;
+  const size_t tiles_n = size_t(rows_pad_of(N) / 256);
+  return tiles_n > 1 ? t * (1 + tiles_n) : t;
 }
 
 }  // extern "C"
