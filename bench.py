@@ -127,6 +127,97 @@ def unfused_step(layer_u, acts_u, x, y, l1s, l2):
     y.addmm_(t, l2)
 
 
+def mlp_bench(args):
+    """The FLUX MLP pair fc1 (4608 x 3072 -> 12288) -> GELU -> fc2 (12288 -> 3072), r 32, INT4. One
+    step = both layers. Fused: fc1's activation kernel, fc1's GEMM with fc2's activation side in its
+    epilogue (+ the t2 reduction), fc2's GEMM. Unfused: fc1's two kernels writing Y1, fc2's
+    activation kernel applying the GELU as it reads Y1, fc2's GEMM."""
+    import torch
+    import synth
+    import w4a4_quantized_gemm_smooth_amd as w4
+    dev = torch.device("cuda:0")
+    d1, d2 = synth.workload("flux_mlp_fc1"), synth.workload("flux_mlp_fc2")
+    M, K, N, N2, r = d1["M"], d1["K"], d1["N"], d2["N"], d1["rank"]
+    log(f"[bench] flux_mlp: fc1 {M}x{K}->{N}, fc2 ->{N2}, r={r}")
+    lam1, inv1 = w4.smooth_factors(w4.column_absmax(d1["x"]), w4.column_absmax(d1["w"]))
+    lam2, inv2 = w4.smooth_factors(w4.column_absmax(d2["x"]), w4.column_absmax(d2["w"]))
+    fc1 = w4.W4A4Linear(w4.prepare_weights(d1["w"], lam1, r), inv1, device=dev)
+    fc2 = w4.W4A4Linear(w4.prepare_weights(d2["w"], lam2, r), inv2, device=dev)
+    pair = w4.MLPPair(fc1, fc2)
+    x = torch.from_numpy(np.ascontiguousarray(d1["x"]).view(np.int16)).to(dev).view(torch.bfloat16)
+    y2 = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+    ops = layer_ops(M, N, K, r) + layer_ops(M, N2, N, r)
+    stream = torch.cuda.current_stream()
+    b = pair.buffers(M)
+    f1, f2, a2 = fc1, fc2, b["act2"]
+
+    def fused_parts():
+        a1 = f1.quantize(x)
+        yield
+        w4.lowrank_linear_gelu_quant(a1["xq"], a1["xscale"], a1["xl1"], f1.wq, f1.wscale, f1.l2t, f1.bias, M, N, K, r,
+                                     f1.fmt, f2.inv_lambda, f2.l1t, f2.rank, a2["xq"], a2["xscale"], b["xl1_2_fused"])
+        yield
+        f2.gemm(dict(a2, xl1=b["xl1_2_fused"]), M, y2)
+        yield
+
+    def unfused_parts():
+        a1 = f1.quantize(x)
+        yield
+        f1.gemm(a1, M, b["y1"])
+        yield
+        w4.gelu_quantize_act(b["y1"], f2.inv_lambda, f2.l1t, f2.rank, f2.fmt, a2["xq"], a2["xscale"], a2["xl1"])
+        yield
+        f2.gemm(a2, M, y2)
+        yield
+
+    def run(parts, n):
+        for _ in range(n):
+            for _ in parts():
+                pass
+
+    def timed(parts):
+        run(parts, args.warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(parts, args.steps)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        per = []   # per-kernel event times, in a separate pass
+        for _ in range(args.steps):
+            evs = [torch.cuda.Event(enable_timing=True)]
+            evs[0].record(stream)
+            for _ in parts():
+                evs.append(torch.cuda.Event(enable_timing=True))
+                evs[-1].record(stream)
+            per.append(evs)
+        torch.cuda.synchronize()
+        kern = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in per])) for i in range(len(per[0]) - 1)]
+        return ms, kern
+
+    ms_f, k_f = timed(fused_parts)
+    ms_u, k_u = timed(unfused_parts)
+    fc1_ops = layer_ops(M, N, K, r)
+    out = {
+        "metric": "effective TOPS of fused W4A4+rank-32 linear at FLUX shapes; % MFMA peak",
+        "value": round(ops / (ms_f * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_f, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int4", "data": "synthetic (seeded FLUX-shaped MLP pair; random weights)",
+        "config": {"workload": "flux_mlp", "M": M, "K": K, "N": N, "N2": N2, "rank": r, "format": "int4_g64",
+                   "ops_per_step": ops, "path": "fc2's activation side fused into fc1's GEMM epilogue"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<0,2,2>", "achieved": round(fc1_ops / (k_f[1] * 1e-3) / 1e12, 2),
+                     "peak": PEAK_TOPS["int4_g64"], "unit": "TFLOP/s",
+                     "frac": round(fc1_ops / (k_f[1] * 1e-3) / 1e12 / PEAK_TOPS["int4_g64"], 4), "traffic": None,
+                     "avg_launch_ms": round(k_f[1], 5), "algorithmic_ops_per_launch": fc1_ops},
+        "kernels_fused_ms": {"fc1_quantize": round(k_f[0], 5), "fc1_gemm_gelu_quant_and_t2_reduce": round(k_f[1], 5),
+                             "fc2_gemm": round(k_f[2], 5)},
+        "kernels_unfused_ms": {"fc1_quantize": round(k_u[0], 5), "fc1_gemm": round(k_u[1], 5),
+                               "fc2_gelu_quantize": round(k_u[2], 5), "fc2_gemm": round(k_u[3], 5)},
+        "ablation": {"unfused_ms_per_step": round(ms_u, 5), "fused_ms_per_step": round(ms_f, 5),
+                     "fusion_gain_pct": round(100.0 * (ms_u - ms_f) / ms_u, 2)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(d, lam, inv, budget_s=20.0):
     """Time the oracle's forward (quantize X, 4-bit main branch, low-rank branch) on a sample of
     rows; the oracle's weight preparation is offline and not timed."""
@@ -189,6 +280,8 @@ def main():
     import w4a4_quantized_gemm_smooth_amd as w4
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload == "flux_mlp":
+        return mlp_bench(args)
     dev = torch.device("cuda:0")
     d = synth.workload(args.workload)
     if args.batch:
