@@ -852,10 +852,8 @@ hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, 
                      X, M, K, ldx, il, l1t, m_pad, gs, xq, xs, xl1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (FMT == W4A4_FMT_W8A8) {  // per-token scales from the slices' partial maxima, then the codes
-    e = launch_quantize_w8(X, M, K, ldx, il, m_pad, nsl, xq, static_cast<float*>(xs), st);
-    if (e != hipSuccess) return e;
-  }
+  if (FMT == W4A4_FMT_W8A8)  // per-token scales from the slices' partial maxima, the codes, and t
+    return launch_quantize_w8(X, M, K, ldx, il, m_pad, nsl, xq, static_cast<float*>(xs), xl1, NT * 16, st);
   if (NT == 0 || nsl == 1) return hipSuccess;
   const int n = m_pad * NT * 16;
   hipLaunchKernelGGL(t_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, xl1 + n, nsl, n, xl1);

@@ -122,9 +122,9 @@ __device__ __forceinline__ void store_y(v16f (&acc)[I4_MT][2], uint8_t* stage, c
 
 // Launchers of the W8A8 translation unit (asynchronous on `st`; they return the launch status).
 // Per-token INT8 codes and scales from the partial row maxima the activation kernel left behind
-// the scales (nsl planes).
+// the scales (nsl planes); with rank_pad > 0 and nsl > 1 it also sums the partial t planes.
 hipError_t launch_quantize_w8(const uint16_t* X, int M, int K, int ldx, const float* inv_lambda, int m_pad, int nsl,
-                              uint8_t* xq, float* xscale, hipStream_t st);
+                              uint8_t* xq, float* xscale, float* xl1, int rank_pad, hipStream_t st);
 // The W8A8 GEMM with the low-rank up projection and bias in its epilogue; ntr = rank_pad / 16.
 hipError_t dispatch_gemm_w8a8(int ntr, const uint8_t* xq, const float* xscale, const float* xl1, const uint8_t* wq,
                               const float* wscale, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy,

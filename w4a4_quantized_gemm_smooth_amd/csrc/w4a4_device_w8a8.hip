@@ -22,12 +22,14 @@ namespace {
 // with X̂ recomputed from X by the same single fp32 multiply. Block = 16 rows x 1024 K: lane c of a
 // wave owns the 16 values 16 c .. 16 c + 15 of the chunk (1/λ loaded once) and the wave takes rows
 // wave, wave + 4, ... (row-uniform, so the partial maxima are scalar loads). Codes go to the
-// [K/32][m_pad][32] layout as one 16-byte store per lane and row.
+// [K/32][m_pad][32] layout as one 16-byte store per lane and row. The blocks of the first K chunk
+// also sum the slices' partial t planes of their rows (slice order, as t_reduce_kernel).
 constexpr int Q8_ROWS = 16, Q8_KCHUNK = 1024;
 
 __global__ __launch_bounds__(256) void quantize_w8_kernel(const uint16_t* __restrict__ X, int M, int K, int ldx,
                                                           const float* __restrict__ inv_lambda, int m_pad, int nsl,
-                                                          uint8_t* __restrict__ xq, float* __restrict__ xscale) {
+                                                          uint8_t* __restrict__ xq, float* __restrict__ xscale,
+                                                          float* __restrict__ xl1, int rp, int tplanes) {
   const int nkb = (K + Q8_KCHUNK - 1) / Q8_KCHUNK;
   const int rb = blockIdx.x / nkb, kb = blockIdx.x % nkb;
   const int c = threadIdx.x & 63;
@@ -42,6 +44,22 @@ __global__ __launch_bounds__(256) void quantize_w8_kernel(const uint16_t* __rest
     il[4 * q + 1] = v.y;
     il[4 * q + 2] = v.z;
     il[4 * q + 3] = v.w;
+  }
+  if (kb == 0 && tplanes > 0) {  // t of the block's rows = Σ_planes partial t, in plane order
+    const int q4 = rp / 4;
+    for (int idx = threadIdx.x; idx < Q8_ROWS * q4; idx += 256) {
+      const size_t off = (size_t)(rb * Q8_ROWS + idx / q4) * rp + 4 * (idx % q4);
+      const size_t plane = (size_t)m_pad * rp;
+      float4 t = *reinterpret_cast<const float4*>(xl1 + plane + off);
+      for (int p = 1; p < tplanes; ++p) {
+        const float4 v = *reinterpret_cast<const float4*>(xl1 + plane * (1 + p) + off);
+        t.x += v.x;
+        t.y += v.y;
+        t.z += v.z;
+        t.w += v.w;
+      }
+      *reinterpret_cast<float4*>(xl1 + off) = t;
+    }
   }
   const float* part = xscale + m_pad;
 #pragma unroll
@@ -316,10 +334,11 @@ hipError_t launch_gemm_w8a8(const uint8_t* xq, const float* xs, const float* xl1
 namespace w4a4 {
 
 hipError_t launch_quantize_w8(const uint16_t* X, int M, int K, int ldx, const float* inv_lambda, int m_pad, int nsl,
-                              uint8_t* xq, float* xscale, hipStream_t st) {
+                              uint8_t* xq, float* xscale, float* xl1, int rank_pad, hipStream_t st) {
   const int nkb = (K + Q8_KCHUNK - 1) / Q8_KCHUNK;
+  const int tplanes = rank_pad > 0 && nsl > 1 ? nsl : 0;
   hipLaunchKernelGGL(quantize_w8_kernel, dim3(m_pad / Q8_ROWS * nkb), dim3(256), 0, st, X, M, K, ldx, inv_lambda,
-                     m_pad, nsl, xq, xscale);
+                     m_pad, nsl, xq, xscale, xl1, rank_pad, tplanes);
   return hipGetLastError();
 }
 
