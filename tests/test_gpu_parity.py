@@ -310,3 +310,36 @@ def test_full_size_mxfp4_sweep(m):
     check_activation_side(d, inv, ref, d["fmt"], g, rows=m)
     rows = _sample_rows(m, seed=m)
     check_y(g, oracle_rows(d, inv, ref, d["fmt"], rows), rows)
+
+
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
+def test_max_rank(fmt):
+    """The largest supported rank (128: eight 16-rank MFMA steps in both projections)."""
+    m, k, n, r = 300, 256, 300, w4.MAX_RANK
+    d = synth.make_layer(m, k, n, n_outliers=4, outlier_scale=30.0, seed=128)
+    lam, inv = _smooth(d)
+    ref = oracle_weights(d, r, fmt, lam)
+    print(f"[max rank] {fmt} M={m} K={k} N={n} r={r}", flush=True)
+    g = gpu_layer(d, lam, inv, r, fmt, ref, pad_cols=2)
+    check_activation_side(d, inv, ref, fmt, g)
+    check_y(g, O.linear(d["x"], inv, ref)["y"])
+
+
+def test_w8a8_largest_k():
+    """W8A8 at the largest K whose int32 dot products cannot overflow (127² · 131072 < 2^31), with
+    rows of near-full-scale codes so that the exact sums come close to the limit."""
+    m, k, n = 40, w4.W8A8_MAX_K, 24
+    rng = np.random.default_rng(31)
+    x = np.sign(rng.standard_normal((m, k))).astype(np.float32)        # ±1: every code ±127
+    w = (np.sign(rng.standard_normal((n, k))) * 0.02).astype(np.float32)
+    x[:4] = 1.0                                                        # rows whose products all align
+    w[:4] = 0.02
+    d = dict(x=synth.f32_to_bf16_bits(x), w=synth.f32_to_bf16_bits(w))
+    lam = np.ones(k, np.float32)
+    ref = O.prepare_weights(d["w"], lam, 0, "w8a8")
+    assert np.abs(ref["cw"]).max() == 127
+    print(f"[w8a8 max K] M={m} K={k} N={n}", flush=True)
+    g = gpu_layer(d, lam, lam, 0, "w8a8", ref)
+    act = check_activation_side(d, lam, ref, "w8a8", g)
+    assert np.abs(act["cx"]).min() == 127
+    check_y(g, O.linear(d["x"], lam, ref)["y"])
