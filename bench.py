@@ -9,8 +9,9 @@ low-rank up projection. Prints ONE JSON line on stdout (diagnostics go to stderr
   value      effective TOPS = (2·M·N·K + 2·M·r·(K+N)) / time per step (whole job, one GPU)
   roofline   the GEMM kernel: algorithmic ops per launch / its average launch time (HIP events on
              the launch stream around each GEMM launch of `steps` further steps, right after the
-             timed region) against the MI355X dense int8/fp8 MFMA peak (5.0 POP/s) for INT4,
-             or the MXFP4 peak (10.1 PFLOP/s) for the FP4 variant
+             timed region) against the MI355X dense int8/fp8 MFMA peak (5.0 POP/s) for INT4 and
+             W8A8, or the MXFP4 peak (10.1 PFLOP/s) for the FP4 variant; also against the peak
+             measured on this GPU by register-only MFMA chains (libw4a4_peak.so)
   cpu_baseline  the numpy oracle's forward pass on a bounded sample of rows of the same layer
 """
 from __future__ import annotations
@@ -51,7 +52,7 @@ def quantize_bytes(M, K, r, fmt):
 
 def gemm_kernel_name(fmt, rank_pad):
     nt = rank_pad // 16
-    return f"gemm_w8a8_kernel<{nt}>" if fmt == "w8a8" else f"gemm_kernel<{0 if fmt == 'int4_g64' else 1},{nt}>"
+    return f"gemm_w8a8_kernel<{nt}>" if fmt == "w8a8" else f"gemm_kernel<{0 if fmt == 'int4_g64' else 1},{nt},-1>"
 
 
 def time_layer(lay, x, y, M, steps, warmup):
@@ -125,6 +126,67 @@ def unfused_step(layer_u, acts_u, x, y, l1s, l2):
     layer_u.gemm(acts_u, M, y)
     t = torch.matmul(x, l1s)
     y.addmm_(t, l2)
+
+
+def measured_peaks(dev):
+    """Measured MFMA peaks (TOPS) from libw4a4_peak.so: register-only chains of one instruction per
+    kind on every SIMD; None when the helper library is absent."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "w4a4_quantized_gemm_smooth_amd", "libw4a4_peak.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.w4a4_peak_mfma_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.w4a4_peak_mfma_launch.restype = ctypes.c_int
+    L.w4a4_peak_mfma_macs.argtypes = [ctypes.c_int]
+    L.w4a4_peak_mfma_macs.restype = ctypes.c_longlong
+    blocks, iters = 2048, 1000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for kind, name in ((0, "int8"), (1, "fp6"), (2, "fp4"), (3, "bf16")):
+        launch = lambda: L.w4a4_peak_mfma_launch(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                                 ctypes.c_void_p(stream.cuda_stream))
+        assert launch() == 0
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert launch() == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        ops = 2.0 * blocks * 4 * iters * 8 * L.w4a4_peak_mfma_macs(kind)
+        res[name] = round(ops / (best * 1e-3) / 1e12, 1)
+    del out
+    return res
+
+
+def copy_bandwidth(dev, mib=256):
+    """Read + write GB/s of a device-to-device copy of `mib` MiB (best of 3)."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    dst.copy_(src)
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return 2.0 * (mib << 20) / (best * 1e-3) / 1e9
+
+
+def pct(v, q):
+    return round(float(np.percentile(np.asarray(v), q)), 5)
 
 
 def mlp_bench(args):
@@ -356,6 +418,9 @@ def main():
     value = ops / (ms_step * 1e-3) / 1e12
     achieved = ops / (g_avg * 1e-3) / 1e12
     peak = PEAK_TOPS[fmt]
+    peaks = measured_peaks(dev)
+    peak_meas = None if peaks is None else peaks["fp4" if fmt == "mxfp4_b32" else "int8"]
+    copy_gbs = copy_bandwidth(dev)
     qbytes = quantize_bytes(M, K, r, fmt)
     traffic = traffic_from_profile(os.path.join(ROOT, "w4a4_quantized_gemm_smooth_amd", "csrc", "w4a4_device.hip")) \
         if args.workload == "flux_qkv" and fmt == "int4_g64" else None
@@ -369,14 +434,21 @@ def main():
         "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(fmt, prep["rank_pad"]),
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "avg_launch_ms": round(g_avg, 5), "algorithmic_ops_per_launch": ops},
+                     "avg_launch_ms": round(g_avg, 5), "algorithmic_ops_per_launch": ops,
+                     "peak_measured": peak_meas,
+                     "frac_measured": None if not peak_meas else round(achieved / peak_meas, 4),
+                     "measured_mfma_peaks_TOPS": peaks},
         "kernels": {
             "quantize_act": {"avg_ms_warm": round(q_avg, 5), "avg_ms_cold": round(float(np.mean(cq)), 5),
+                             "cold_median_p10_p90_ms": [pct(cq, 50), pct(cq, 10), pct(cq, 90)],
                              "algorithmic_bytes": qbytes,
-                             "GB/s_cold": round(qbytes / (np.mean(cq) * 1e-3) / 1e9, 1),
-                             "hbm_frac_cold": round(qbytes / (np.mean(cq) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                             "GB/s_cold": round(qbytes / (np.median(cq) * 1e-3) / 1e9, 1),
+                             "hbm_frac_cold": round(qbytes / (np.median(cq) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "copy_GB/s_measured": round(copy_gbs, 1),
+                             "frac_of_copy_cold": round(qbytes / (np.median(cq) * 1e-3) / 1e9 / copy_gbs, 4)},
             "gemm": {"avg_ms_warm": round(g_avg, 5), "avg_ms_cold": round(float(np.mean(cg)), 5),
-                     "TOPS_cold": round(ops / (np.mean(cg) * 1e-3) / 1e12, 2)},
+                     "cold_median_p10_p90_ms": [pct(cg, 50), pct(cg, 10), pct(cg, 90)],
+                     "TOPS_cold": round(ops / (np.median(cg) * 1e-3) / 1e12, 2)},
         },
     }
     if not args.no_ablation and r > 0:

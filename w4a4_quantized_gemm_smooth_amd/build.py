@@ -17,6 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libw4a4.so")
+PEAK_LIB = os.path.join(PKG, "libw4a4_peak.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -59,6 +60,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # the benchmark's measured-MFMA-peak helper (not part of the layer's library)
+    tmp = PEAK_LIB + ".tmp"
+    _run([HIPCC, *DEVICE_FLAGS, "-shared", os.path.join(CSRC, "peak_mfma.hip"), "-o", tmp], verbose)
+    os.replace(tmp, PEAK_LIB)
     return LIB
 
 
