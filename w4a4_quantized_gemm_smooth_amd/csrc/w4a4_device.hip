@@ -837,6 +837,188 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
   }
 }
 
+// ===================================================================================
+// Kernel 2b: the MXFP4 GEMM on 128 x 128 blocks, for grids with fewer 256 x 256 tiles than the
+// GPU has compute units (small M: K = N = 3072 at M = 1024 is 48 large tiles for 256 CUs). Four
+// waves as 2 x 2, each 64 x 64 (2 x 2 tiles of 32x32); a ring of 8 slots of 9 KB, so two blocks
+// share a CU (the kernel runs when one round of blocks covers the grid; a 16-slot ring, one block per
+// CU, measured no faster at M = 1024). Otherwise the large kernel's MXFP4 path: codes and E8M0
+// block scales copied by the LDS DMA path six groups ahead, one barrier per two groups, the scaled
+// MFMA applying the block
+// scales, the low-rank up projection first (t and L2 straight from global memory), Y through LDS.
+// Groups past the end of K are zero-filled by pointing the copy's lane offset past the buffer's
+// range (a raw buffer load outside num_records returns zeros): zero codes add exactly 0.
+// ===================================================================================
+constexpr int MX_BM = 128, MX_THREADS = 256, MX_MT = 2;
+constexpr int MX_NS = 8;            // ring slots (groups); even
+constexpr int MX_SMALL_GRID = 512;  // the 128 x 128 kernel runs when its grid is at most this
+
+struct MxSlot {
+  uint8_t a[128 * 32];
+  uint8_t b[128 * 32];
+  uint8_t s[512];    // E8M0: A block 2g (128 rows), A block 2g+1, B block 2g, B block 2g+1
+  uint8_t pad[512];  // 9 KB: room for a wave's 64 x 144-byte Y staging
+};
+
+template <int NTR>  // NTR = rank_pad / 16
+__global__ __launch_bounds__(MX_THREADS, 2) void gemm_mx_small_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ xl1,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
+    int m_pad, int n_pad) {
+  __shared__ __attribute__((aligned(16))) MxSlot sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7;
+  MxSlot* const ring[MX_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5, &sl6, &sl7};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, m_pad / MX_BM, n_pad / MX_BM, tm, tn);
+  const int m0 = tm * MX_BM, n0 = tn * MX_BM;
+  const int G = K / W4A4_GROUP;
+
+  // code DMA: wave w fills bytes [1024 w, 1024 w + 1024) of an operand's 4 KB, lane i the 16 B of
+  // row 32 w + i / 2 that the swizzle puts there
+  const int drow = 32 * wave + (lane >> 1);
+  const int c_lane = drow * 32 + 16 * ((lane & 1) ^ ((drow >> 3) & 1));
+  constexpr int RSRC_W3 = 0x00020000;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(xq + (size_t)m0 * 32), 0, (G * m_pad - m0) * 32, RSRC_W3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wq + (size_t)n0 * 32), 0, (G * n_pad - n0) * 32, RSRC_W3);
+  // scale DMA: the 256 B of A (even waves) or B (odd waves; waves 2 and 3 repeat 0 and 1): lanes
+  // 0..31 the 128 rows of block 2g, lanes 32..63 those of block 2g + 1 (planes [K/32][rows])
+  const bool s_is_a = (wave & 1) == 0;
+  const int s_rows = s_is_a ? m_pad : n_pad, s_row0 = s_is_a ? m0 : n0;
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>((s_is_a ? xs : ws) + s_row0), 0, (K / W4A4_MX_BLOCK) * s_rows - s_row0, RSRC_W3);
+  const int s_lane = (lane >> 5) * s_rows + 4 * (lane & 31);
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto dma = [&](int g, MxSlot* sl) {  // 3 vector-memory instructions per wave and group
+    const int oob = g < G ? 0 : (int)0x80000000;
+    g = min(g, G - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr)(sl->a + 1024 * wave), 16, c_lane | oob, g * m_pad * 32, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr)(sl->b + 1024 * wave), 16, c_lane | oob, g * n_pad * 32, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr)(sl->s + 256 * (wave & 1)), 4, s_lane, g * 2 * s_rows, 0, 0);
+  };
+
+  v16f acc[MX_MT][2];
+#pragma unroll
+  for (int i = 0; i < MX_MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+  const int lr = lane & 31, lh = lane >> 5;
+  const int arow0 = wm * 64 + lr, bcol0 = wn * 64 + lr;
+
+  // low-rank up projection first: acc = bf16(t)·L2 (32x32x16 bf16 MFMAs), 32 ranks per batch of
+  // register loads; the first batch is issued before the ring's copies and lands under the
+  // prologue's wait
+  constexpr int RP = NTR * 16;
+  v4i LB[2][2];
+  float4 tv[2][MX_MT][2];
+  auto lr_load = [&](int k0) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kk = k0 + 16 * s;
+      if (kk >= RP) break;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        LB[s][j] = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + bcol0 + j * 32) * RP + kk + 8 * lh);
+#pragma unroll
+      for (int i = 0; i < MX_MT; ++i) {
+        const float* tp = xl1 + (size_t)(m0 + arow0 + i * 32) * RP + kk + 8 * lh;
+        tv[s][i][0] = *reinterpret_cast<const float4*>(tp);
+        tv[s][i][1] = *reinterpret_cast<const float4*>(tp + 4);
+      }
+    }
+  };
+  auto lr_mfma = [&](int k0) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (k0 + 16 * s >= RP) break;
+#pragma unroll
+      for (int i = 0; i < MX_MT; ++i) {
+        const float4 t0 = tv[s][i][0], t1 = tv[s][i][1];
+        const v4i TA = v4i{(int)pack_bf16x2(t0.x, t0.y), (int)pack_bf16x2(t0.z, t0.w), (int)pack_bf16x2(t1.x, t1.y),
+                           (int)pack_bf16x2(t1.z, t1.w)};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(TA), as_bf16x8(LB[s][j]), acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  if (NTR > 0) lr_load(0);
+#pragma unroll
+  for (int s = 0; s < MX_NS - 2; ++s) dma(s, ring[s]);
+  wait_vmcnt<3 * (MX_NS - 3)>();  // the low-rank operands and group 0 have landed
+  __builtin_amdgcn_s_barrier();
+  if (NTR > 0) {
+    lr_mfma(0);
+#pragma unroll
+    for (int k0 = 32; k0 < RP; k0 += 32) {  // larger ranks: later batches wait for their loads
+      lr_load(k0);
+      wait_vmcnt<0>();
+      lr_mfma(k0);
+    }
+  }
+
+  const int a_off = sw_off32(arow0, lh), b_off = sw_off32(bcol0, lh);
+  // operands of group g + 1 are read at the start of group g (double-buffered registers)
+  auto rd = [&](const MxSlot* sl, v4i (&A)[MX_MT], v4i (&B)[2], int (&sA)[MX_MT], int (&sB)[2]) {
+#pragma unroll
+    for (int i = 0; i < MX_MT; ++i) {
+      A[i] = *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i);
+      sA[i] = sl->s[128 * lh + arow0 + 32 * i];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      B[j] = *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j);
+      sB[j] = sl->s[256 + 128 * lh + bcol0 + 32 * j];
+    }
+  };
+  auto op8 = [](v4i v) { return v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0}; };
+  v4i A[2][MX_MT], B[2][2];
+  int sA[2][MX_MT], sB[2][2];
+  rd(ring[0], A[0], B[0], sA[0], sB[0]);
+  for (int g0 = 0; g0 < G; g0 += MX_NS) {
+#pragma unroll
+    for (int u = 0; u < MX_NS; ++u) {
+      const int g = g0 + u, c = u & 1;
+      if (u % 2 == 0) {
+        // groups g+1 and g+2 have landed; everyone is done with slots g-2 and g-1
+        wait_vmcnt<3 * (MX_NS - 5)>();
+        __builtin_amdgcn_s_barrier();
+        dma(g + MX_NS - 2, ring[(u + MX_NS - 2) % MX_NS]);
+        dma(g + MX_NS - 1, ring[(u + MX_NS - 1) % MX_NS]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      rd(ring[(u + 1) % MX_NS], A[c ^ 1], B[c ^ 1], sA[c ^ 1], sB[c ^ 1]);
+#pragma unroll
+      for (int t = 0; t < 2 * MX_MT; ++t) {
+        const int i = t >> 1, j = t & 1;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8(A[c][i]), op8(B[c][j]), acc[i][j], 4, 4, 0,
+                                                                  sA[c][i], 0, sB[c][j]);
+      }
+      // the next group's LDS reads issue between this group's MFMAs
+#pragma unroll
+      for (int q = 0; q < 2 * MX_MT; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // the rest of the reads
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<0>();  // no LDS DMA may outlive the block
+  __builtin_amdgcn_s_barrier();
+  uint8_t* stage = reinterpret_cast<uint8_t*>(ring[0]);
+#pragma unroll
+  for (int w = 1; w < 4; ++w)
+    if (wave == w) stage = reinterpret_cast<uint8_t*>(ring[w]);  // wave-uniform select
+  static_assert(64 * Y_ES <= (int)sizeof(MxSlot), "staging fits a ring slot");
+  store_y(acc, stage, bias, Y, ldy, M, N, m0 + wm * 64, n0 + wn * 64, lane);
+}
+
 // ----------------------------------------------------------------------------- launch helpers
 template <int FMT, int NT, bool GELU_IN = false>
 hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, const uint16_t* l1t, int m_pad,
@@ -883,6 +1065,9 @@ hipError_t launch_gemm(int fmt, const uint8_t* xq, const void* xs, const float* 
   if (fmt == W4A4_FMT_INT4_G64)
     hipLaunchKernelGGL((gemm_kernel<W4A4_FMT_INT4_G64, NTR>), grid, block, 0, st, xq, xsb, xl1, wq, wsb, l2t, bias, Y,
                        ldy, M, N, K, m_pad, n_pad, GeluQuantArgs{});
+  else if ((m_pad / MX_BM) * (n_pad / MX_BM) <= MX_SMALL_GRID)  // one round of small blocks (2 per CU) covers it
+    hipLaunchKernelGGL((gemm_mx_small_kernel<NTR>), dim3((m_pad / MX_BM) * (n_pad / MX_BM)), dim3(MX_THREADS), 0, st,
+                       xq, xsb, xl1, wq, wsb, l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
   else
     hipLaunchKernelGGL((gemm_kernel<W4A4_FMT_MXFP4_B32, NTR>), grid, block, 0, st, xq, xsb, xl1, wq, wsb, l2t, bias,
                        Y, ldy, M, N, K, m_pad, n_pad, GeluQuantArgs{});

@@ -69,14 +69,16 @@ __device__ __forceinline__ void tile_of(int b, int nblocks, int tiles_m, int til
   tn = in_group / gsize;
 }
 
-// Y store shared by the GEMMs: the wave's 128 x 64 block of fp32 results (+ bias) -> bf16 Y
-// through LDS, so that every lane writes whole 16-byte row segments. The block goes out in two
-// halves of 64 rows, staged in `stage` (an idle ring slot of the wave) with a 144-byte row stride
+// Y store shared by the GEMMs: the wave's (32 MT) x 64 block of fp32 results (+ bias) -> bf16 Y
+// through LDS, so that every lane writes whole 16-byte row segments. The block goes out in pieces
+// of 64 rows, staged in `stage` (an idle ring slot of the wave, 9 KB) with a 144-byte row stride
 // (conflict-free 2-byte writes and 16-byte reads). The 32x32 MFMA output layout: lane holds column
 // lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4. r0, c0: first row and column of the wave's block.
 constexpr int Y_ES = 144;
-__device__ __forceinline__ void store_y(v16f (&acc)[I4_MT][2], uint8_t* stage, const uint16_t* bias, uint16_t* Y,
+template <int MT>
+__device__ __forceinline__ void store_y(v16f (&acc)[MT][2], uint8_t* stage, const uint16_t* bias, uint16_t* Y,
                                         int ldy, int M, int N, int r0, int c0, int lane) {
+  static_assert(MT % 2 == 0, "pieces of 64 rows");
   const int lr = lane & 31, lh = lane >> 5;
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(Y) & 15u) == 0) && (ldy % 8 == 0);
   float bcol[2];
@@ -86,7 +88,7 @@ __device__ __forceinline__ void store_y(v16f (&acc)[I4_MT][2], uint8_t* stage, c
     bcol[j] = (bias && col < N) ? bf16f(bias[col]) : 0.f;
   }
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < MT / 2; ++half) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
