@@ -1,5 +1,9 @@
 // Device half of libw4a4 for gfx950 (CDNA4): the fused activation quantizer with the low-rank
-// down projection, and the 4-bit GEMMs with the low-rank up projection in the epilogue.
+// down projection, and the 4-bit GEMMs with the low-rank up projection in the epilogue; also the
+// first pass of the 8-bit setting's activation side (partial row maxima; the rest of the W8A8 path
+// is in w4a4_device_w8a8.hip), the MLP pair's GELU (in the activation kernel, or in fc1's GEMM
+// epilogue together with fc2's whole activation side), and the MXFP4 GEMM on 128 x 128 blocks for
+// small grids. The device-side C ABI entry points are at the end of this file.
 //
 // Method: SVDQuant summary page (arXiv 2411.05007v4) §4.2 (smoothing, low-rank branch,
 // quantized residual), §4.3 / Fig. 6 (the down projection shares X̂ with the quantizer; the up
@@ -101,7 +105,8 @@ __device__ __forceinline__ uint2 quant_int4_lane(const float (&xh)[2][8], uint32
 }
 
 // ===================================================================================
-// Kernel 1: activation side. Per row and group: X̂ = fp32(x * inv_lambda); codes + scales;
+// Kernel 1: activation side. Per row and group: X̂ = fp32(x * inv_lambda); codes + scales (W8A8:
+// the row's running max|X̂| instead, written per slice for the second W8A8 pass);
 // t += bf16(X̂) · L1 (MFMA). One block = 128 rows (8 waves of 16) x one slice of at most
 // QA_MAX_GS groups: every wave issues the X loads of all its groups at once, and the slice's
 // 1/λ and L1 rows are copied into LDS by the LDS DMA path, shared by the 8 row tiles. With
