@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define W4A4_ABI_VERSION 1
+#define W4A4_ABI_VERSION 2   /* 2: + W8A8 format, refined preparation, the MLP-pair GELU calls */
 #define W4A4_GROUP 64        /* INT4 group size along K (App. D) */
 #define W4A4_MX_BLOCK 32     /* FP4 block size along K */
 #define W4A4_ROW_ALIGN 256   /* M and N are padded to a multiple of this in library layouts */

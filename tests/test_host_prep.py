@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     L = w4.lib()
     missing = [n for n in decl if not hasattr(L, n)]
     assert not missing, missing
-    assert L.w4a4_abi_version() == 1
+    assert L.w4a4_abi_version() == 2
 
 
 def test_single_hip_runtime_in_process():
