@@ -547,10 +547,24 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   auto a_raw = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i); };
   auto b_raw = [&](const I4Slot* sl, int j) { return *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j); };
   if constexpr (INT4) {
-  // operands of the scale outer product: the A side is the bf16 scale of the lane's row in every
-  // lane; the B side is the scale at k = 0 (lanes 0..31) and zero for k = 4 (lanes 32..63, read
-  // from the slot's zero words), and zero for groups past the end, so S = s_x s_w exactly. Kept as
-  // one zero-extended register, widened at the MFMA.
+  // Row rotation against VGPR bank conflicts. The FMA acc[v] += p[v] * sc[v] would read three
+  // registers with the same index in three tuples that the allocator places at the same alignment,
+  // i.e. three times the same bank. Instead the lane that supplies A row rho of the FP6 MFMA loads
+  // row rot(rho, 2), and of the scale MFMA row rot(rho, 1), where rot(rho, k) is the row that the
+  // 32x32 output layout (register u = 4 (rho / 8) + rho % 4 of lane half (rho / 4) % 2) puts k
+  // registers earlier. Row rho of the tile then sits in register v of acc, v + 2 of p and v + 1 of
+  // sc: three different banks, same arithmetic.
+  auto rot = [](int rho, int k) {
+    const int u = ((((rho >> 3) << 2) | (rho & 3)) - k) & 15;
+    return ((u >> 2) << 3) | (rho & 4) | (u & 3);
+  };
+  const int a_off4 = sw_off32(wm * 128 + rot(lr, 2), lh);
+  const int srow0 = wm * 128 + rot(lr, 1);
+  auto a_raw4 = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off4 + 1024 * i); };
+  // operands of the scale outer product: the A side is the bf16 scale of the lane's (rotated) row
+  // in every lane; the B side is the scale at k = 0 (lanes 0..31) and zero for k = 4 (lanes
+  // 32..63, read from the slot's zero words), and zero for groups past the end, so S = s_x s_w
+  // exactly. Kept as one zero-extended register, widened at the MFMA.
   const int sb_lane_off = lh ? (int)offsetof(I4Slot, z) : (int)offsetof(I4Slot, s) + 2 * (256 + bcol0);
   auto sa_val = [&](const I4Slot* sl, int row) -> uint32_t { return sl->s[row]; };
   auto sb_val = [&](const I4Slot* sl, int j, bool live) -> uint32_t {
@@ -570,10 +584,10 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     Bv[j] = unfold_fp6(b_raw(ring[0], j));
     OB[j] = sb_val(ring[0], j, true);
   }
-  Av = unfold_fp6(a_raw(ring[0], 0));
-  OA = sa_val(ring[0], arow0);
-  An_raw = a_raw(ring[0], 1);
-  OAn = sa_val(ring[0], arow0 + 32);
+  Av = unfold_fp6(a_raw4(ring[0], 0));
+  OA = sa_val(ring[0], srow0);
+  An_raw = a_raw4(ring[0], 1);
+  OAn = sa_val(ring[0], srow0 + 32);
 
   constexpr int T = 2 * I4_MT;
   v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[0], zero16, 2, 2, 0, 130, 0, 130);
@@ -617,12 +631,12 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
         __builtin_amdgcn_sched_barrier(0);
         if (j1 == 0) {  // prefetch the following row's A operand
           if (t1 < T - 2) {
-            An_raw = a_raw(cur, i1 + 1);
-            OAn = sa_val(cur, arow0 + 32 * (i1 + 1));
+            An_raw = a_raw4(cur, i1 + 1);
+            OAn = sa_val(cur, srow0 + 32 * (i1 + 1));
           } else {  // rows 0 and 1 of the next group follow rows 3 and 0
             const int r1 = t1 == T - 2 ? 0 : 1;
-            An_raw = a_raw(nxt, r1);
-            OAn = sa_val(nxt, arow0 + 32 * r1);
+            An_raw = a_raw4(nxt, r1);
+            OAn = sa_val(nxt, srow0 + 32 * r1);
           }
         }
         if (t1 == T - 2) {  // next group's B operands and scales
@@ -640,7 +654,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc[v], acc[i][j][v]);
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[(v + 2) & 15], sc[(v + 1) & 15], acc[i][j][v]);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
         sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sc_op(OA), sc_op(OB[j1]), zero16, 0, 0, 0);
