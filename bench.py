@@ -50,9 +50,15 @@ def quantize_bytes(M, K, r, fmt):
     return M * K * 2 + K * 4 + r * K * 2 + M * (K // 2 + scale_bytes + r * 4)
 
 
-def gemm_kernel_name(fmt, rank_pad):
+def gemm_kernel_name(fmt, rank_pad, M, N):
+    """The GEMM kernel the library launches for this layer (as rocprofv3 names it)."""
     nt = rank_pad // 16
-    return f"gemm_w8a8_kernel<{nt}>" if fmt == "w8a8" else f"gemm_kernel<{0 if fmt == 'int4_g64' else 1},{nt},-1>"
+    if fmt == "w8a8":
+        return f"gemm_w8a8_kernel<{nt}, false>"
+    if fmt == "int4_g64":
+        return f"gemm_kernel<0, {nt}, -1>"
+    small = ((M + 255) // 256 * 2) * ((N + 255) // 256 * 2) <= 512   # grid of 128 x 128 blocks
+    return f"gemm_mx_small_kernel<{nt}>" if small else f"gemm_w8a8_kernel<{nt}, true>"
 
 
 def time_layer(lay, x, y, M, steps, warmup):
@@ -431,7 +437,7 @@ def main():
         "dtype": DTYPE[fmt], "data": "synthetic (seeded FLUX-shaped layer; random weights)",
         "config": {"workload": args.workload, "M": M, "K": K, "N": N, "rank": r, "format": fmt,
                    "ops_per_step": ops, "peak_frac_of_step": round(value / peak, 4)},
-        "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(fmt, prep["rank_pad"]),
+        "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(fmt, prep["rank_pad"], M, prep["N"]),
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "avg_launch_ms": round(g_avg, 5), "algorithmic_ops_per_launch": ops,

@@ -3,7 +3,8 @@
 // first pass of the 8-bit setting's activation side (partial row maxima; the rest of the W8A8 path
 // is in w4a4_device_w8a8.hip), the MLP pair's GELU (in the activation kernel, or in fc1's GEMM
 // epilogue together with fc2's whole activation side), and the MXFP4 GEMM on 128 x 128 blocks for
-// small grids. The device-side C ABI entry points are at the end of this file.
+// small grids (larger MXFP4 grids run the MXFP4 mode of the INT8 GEMM in w4a4_device_w8a8.hip).
+// The device-side C ABI entry points are at the end of this file.
 //
 // Method: SVDQuant summary page (arXiv 2411.05007v4) §4.2 (smoothing, low-rank branch,
 // quantized residual), §4.3 / Fig. 6 (the down projection shares X̂ with the quantizer; the up
@@ -301,17 +302,15 @@ __global__ __launch_bounds__(256) void t_reduce_kernel(const float* __restrict__
 }
 
 // ===================================================================================
-// Kernel 2: the 4-bit GEMM + low-rank up projection (+ bias), bf16 out, INT4 or MXFP4.
+// Kernel 2: the INT4 GEMM + low-rank up projection (+ bias), bf16 out.
 //
 // Block tile 256 (M) x 256 (N), 8 waves as 2 (M) x 4 (N); each wave owns a 4 x 2 grid of 32x32
 // tiles. One K step = one 64-wide group. The codes and scales of each group are copied global ->
 // LDS by the LDS DMA path (global_load_lds) into a ring of I4_NS slots, issued four groups before
 // their first reader; one barrier per two groups publishes the next slots.
-//  * INT4: per group each wave unfolds its A and B operands to FP6 and runs, per tile, one FP6 MFMA
-//    with E8M0 scales 2^3 x 2^3 (the exact integer dot product of the group), one bf16 MFMA (the
-//    exact outer product s_x s_w of the raw bf16 scales) and 16 FMAs into its fp32 accumulators.
-//  * MXFP4: one FP4 MFMA per tile with the E8M0 block scales as its operand scales, accumulating
-//    in place.
+// Per group each wave unfolds its A and B operands to FP6 and runs, per tile, one FP6 MFMA with
+// E8M0 scales 2^3 x 2^3 (the exact integer dot product of the group), one bf16 MFMA (the exact
+// outer product s_x s_w of the raw bf16 scales) and 16 FMAs into its fp32 accumulators.
 // The epilogue adds bf16(t)·L2 and the bias and writes Y through LDS in 16-byte row segments.
 // ===================================================================================
 constexpr int I4_THREADS = 512;
@@ -357,7 +356,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
     int m_pad, int n_pad, GeluQuantArgs fa) {
-  constexpr bool INT4 = FMT == W4A4_FMT_INT4_G64;
+  static_assert(FMT == W4A4_FMT_INT4_G64, "MXFP4 runs on gemm_mx_small_kernel and gemm_w8a8_kernel<., true>");
   __shared__ __attribute__((aligned(16))) I4Slot sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7;
   I4Slot* const ring[I4_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5, &sl6, &sl7};
 
@@ -372,9 +371,8 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   // ---- DMA sources. Instruction w of an operand fills LDS bytes [1024 w, 1024 w + 1024) of the
   // slot, lane i the 16 bytes at 1024 w + 16 i = row 32 w + i / 2, stored half i & 1; the lane
   // loads the global half that the swizzle puts there. Scales: wave w copies 256 bytes, chunk
-  // w & 3 of the slot's 1 KB of scales; waves w and w + 4 write the same bytes. INT4: bf16 scales
-  // of A rows 0..127, A rows 128..255, B rows 0..127, B rows 128..255. MXFP4: E8M0 bytes of A block
-  // 2g, A block 2g+1, B block 2g, B block 2g+1 (256 rows each).
+  // w & 3 of the slot's 1 KB of scales (waves w and w + 4 write the same bytes): the bf16 scales
+  // of A rows 0..127, A rows 128..255, B rows 0..127, B rows 128..255.
   const int drow = 32 * wave + (lane >> 1);
   const int dhalf = (lane & 1) ^ ((drow >> 3) & 1);
   const int c_lane = drow * 32 + 16 * dhalf;   // byte offset of the lane's 16 B in a code tile
@@ -387,13 +385,12 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
       const_cast<uint8_t*>(xq + (size_t)m0 * 32), 0, (G * m_pad - m0) * 32, RSRC_W3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(wq + (size_t)n0 * 32), 0, (G * n_pad - n0) * 32, RSRC_W3);
-  // scale chunk of this wave: INT4 bf16 rows [128 c, 128 c + 128) of A (c = sblk) or B (c = sblk - 2);
-  // MXFP4 E8M0 plane (2g + c) of A or B, 256 rows
+  // scale chunk of this wave: bf16 rows [128 c, 128 c + 128) of A (c = sblk) or B (c = sblk - 2)
   const bool s_is_a = sblk < 2;
   const int s_rows = s_is_a ? m_pad : n_pad, s_row0 = s_is_a ? m0 : n0, sc_ = s_is_a ? sblk : sblk - 2;
   const uint8_t* s_buf = s_is_a ? xs : ws;
-  const int s_first = INT4 ? 2 * (s_row0 + 128 * sc_) : sc_ * s_rows + s_row0;           // bytes
-  const int s_gstride = 2 * s_rows;  // bytes per group: one bf16 per row, or two E8M0 planes
+  const int s_first = 2 * (s_row0 + 128 * sc_);  // bytes
+  const int s_gstride = 2 * s_rows;              // bytes per group: one bf16 per row
   const int s_total = G * s_gstride;
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(s_buf + s_first), 0, s_total - s_first, RSRC_W3);
@@ -546,7 +543,6 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   }
   auto a_raw = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i); };
   auto b_raw = [&](const I4Slot* sl, int j) { return *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j); };
-  if constexpr (INT4) {
   // Row rotation against VGPR bank conflicts. The FMA acc[v] += p[v] * sc[v] would read three
   // registers with the same index in three tuples that the allocator places at the same alignment,
   // i.e. three times the same bank. Instead the lane that supplies A row rho of the FP6 MFMA loads
@@ -660,52 +656,6 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
         sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sc_op(OA), sc_op(OB[j1]), zero16, 0, 0, 0);
         __builtin_amdgcn_s_setprio(0);
         p = pn;
-      }
-    }
-  }
-  } else {
-    // ---- MXFP4: E2M1 x E2M1 with the E8M0 block scales applied by the MFMA (lane half h of a row
-    // is K block 2g + h), accumulating in place; no group epilogue. All operands of group g + 1 are
-    // read from LDS at the start of group g (double-buffered registers), a whole group ahead.
-    // Groups past the end read their (stale) slot with A forced to +0 codes: they add exactly 0.
-    auto rd = [&](const I4Slot* sl, bool live, v4i (&A)[I4_MT], v4i (&B)[2], int (&sA)[I4_MT], int (&sB)[2]) {
-      const uint8_t* sc = reinterpret_cast<const uint8_t*>(sl->s);
-#pragma unroll
-      for (int i = 0; i < I4_MT; ++i) {
-        const v4i a = a_raw(sl, i);
-        A[i] = live ? a : v4i{0, 0, 0, 0};
-        sA[i] = sc[256 * lh + arow0 + 32 * i];
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        B[j] = b_raw(sl, j);
-        sB[j] = sc[512 + 256 * lh + bcol0 + 32 * j];
-      }
-    };
-    auto op8 = [](v4i v) { return v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0}; };
-    v4i A[2][I4_MT], B[2][2];
-    int sA[2][I4_MT], sB[2][2];
-    rd(ring[0], true, A[0], B[0], sA[0], sB[0]);
-    for (int g0 = 0; g0 < G; g0 += I4_NS) {
-#pragma unroll
-      for (int u = 0; u < I4_NS; ++u) {
-        const int g = g0 + u, c = u & 1;
-        if (u % 2 == 0) {
-          wait_vmcnt<3 * (I4_NS - 5)>();
-          __builtin_amdgcn_s_barrier();
-          dma(g + I4_NS - 2, ring[(u + I4_NS - 2) % I4_NS]);
-          dma(g + I4_NS - 1, ring[(u + I4_NS - 1) % I4_NS]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        rd(ring[(u + 1) % I4_NS], g + 1 < G, A[c ^ 1], B[c ^ 1], sA[c ^ 1], sB[c ^ 1]);
-        __builtin_amdgcn_sched_barrier(0);  // the next group's reads stay ahead of this group's MFMAs
-#pragma unroll
-        for (int t = 0; t < 2 * I4_MT; ++t) {
-          const int i = t >> 1, j = t & 1;
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8(A[c][i]), op8(B[c][j]), acc[i][j], 4, 4, 0,
-                                                                    sA[c][i], 0, sB[c][j]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -861,10 +811,10 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
 // GPU has compute units (small M: K = N = 3072 at M = 1024 is 48 large tiles for 256 CUs). Four
 // waves as 2 x 2, each 64 x 64 (2 x 2 tiles of 32x32); a ring of 8 slots of 9 KB, so two blocks
 // share a CU (the kernel runs when one round of blocks covers the grid; a 16-slot ring, one block per
-// CU, measured no faster at M = 1024). Otherwise the large kernel's MXFP4 path: codes and E8M0
-// block scales copied by the LDS DMA path six groups ahead, one barrier per two groups, the scaled
-// MFMA applying the block
-// scales, the low-rank up projection first (t and L2 straight from global memory), Y through LDS.
+// CU, measured no faster at M = 1024; larger grids run the MXFP4 mode of the INT8 GEMM). Codes and
+// E8M0 block scales are copied by the LDS DMA path six groups ahead, one barrier per two groups,
+// the scaled MFMA applies the block scales, the low-rank up projection comes first (t and L2
+// straight from global memory), Y goes out through LDS.
 // Groups past the end of K are zero-filled by pointing the copy's lane offset past the buffer's
 // range (a raw buffer load outside num_records returns zeros): zero codes add exactly 0.
 // ===================================================================================
@@ -1087,9 +1037,8 @@ hipError_t launch_gemm(int fmt, const uint8_t* xq, const void* xs, const float* 
   else if ((m_pad / MX_BM) * (n_pad / MX_BM) <= MX_SMALL_GRID)  // one round of small blocks (2 per CU) covers it
     hipLaunchKernelGGL((gemm_mx_small_kernel<NTR>), dim3((m_pad / MX_BM) * (n_pad / MX_BM)), dim3(MX_THREADS), 0, st,
                        xq, xsb, xl1, wq, wsb, l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
-  else
-    hipLaunchKernelGGL((gemm_kernel<W4A4_FMT_MXFP4_B32, NTR>), grid, block, 0, st, xq, xsb, xl1, wq, wsb, l2t, bias,
-                       Y, ldy, M, N, K, m_pad, n_pad, GeluQuantArgs{});
+  else  // larger grids: the INT8 kernel's structure (copies from one wave per SIMD) on FP4 operands
+    return dispatch_gemm_mx(NTR, xq, xsb, xl1, wq, wsb, l2t, bias, Y, ldy, M, N, K, m_pad, n_pad, st);
   return hipGetLastError();
 }
 

@@ -131,5 +131,9 @@ hipError_t launch_quantize_w8(const uint16_t* X, int M, int K, int ldx, const fl
 hipError_t dispatch_gemm_w8a8(int ntr, const uint8_t* xq, const float* xscale, const float* xl1, const uint8_t* wq,
                               const float* wscale, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy,
                               int M, int N, int K, int m_pad, int n_pad, hipStream_t st);
+// The MXFP4 GEMM on the INT8 kernel's structure (E8M0 block scales applied by the scaled MFMA)
+hipError_t dispatch_gemm_mx(int ntr, const uint8_t* xq, const uint8_t* xscale, const float* xl1, const uint8_t* wq,
+                            const uint8_t* wscale, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy,
+                            int M, int N, int K, int m_pad, int n_pad, hipStream_t st);
 
 }  // namespace w4a4

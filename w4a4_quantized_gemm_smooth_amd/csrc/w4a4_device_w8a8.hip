@@ -5,7 +5,10 @@
 // file holds the code pass and the GEMM.
 //
 // The per-row scales apply once per output, so the GEMM is a plain int8 contraction on
-// v_mfma_i32_32x32x32_i8 with exact int32 accumulation and a scaling epilogue.
+// v_mfma_i32_32x32x32_i8 with exact int32 accumulation and a scaling epilogue. The same GEMM
+// structure also runs the MXFP4 layer on large grids (§3 / App. D FP4 setting: E2M1 codes, E8M0
+// scales per 32-block), one 64-group of FP4 codes being the same 32 bytes per row as an INT8 step
+// and the scaled MFMA applying the block scales.
 
 #include <type_traits>
 
@@ -124,19 +127,34 @@ struct I8Slot {
   uint8_t a[256 * 32];
   uint8_t b[256 * 32];
 };
+// MXFP4 steps (one 64-group of FP4 codes, the same 32 bytes per row as an INT8 step) also carry
+// their E8M0 block scales: A blocks 2g and 2g+1, then B blocks 2g and 2g+1, 256 rows each
+struct MxSlot8 {
+  uint8_t a[256 * 32];
+  uint8_t b[256 * 32];
+  uint8_t s[1024];
+};
 
-template <int NTR>  // NTR = rank_pad / 16
+// MX = true: the same kernel on MXFP4 operands (FP4 E2M1 codes, 32 bytes per row and 64-group,
+// with E8M0 block scales applied by the scaled MFMA; fp32 accumulators, no scale epilogue). The
+// slots then also hold the step's block scales (one more copy per DMA wave and step), and t is
+// read from global memory in the epilogue, which keeps the LDS at 136 KB.
+template <int NTR, bool MX = false>  // NTR = rank_pad / 16
 __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
-    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const float* __restrict__ xl1,
-    const uint8_t* __restrict__ wq, const float* __restrict__ ws, const uint16_t* __restrict__ l2t,
+    const uint8_t* __restrict__ xq, const void* __restrict__ xs_, const float* __restrict__ xl1,
+    const uint8_t* __restrict__ wq, const void* __restrict__ ws_, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K, int m_pad,
     int n_pad) {
+  using Slot = std::conditional_t<MX, MxSlot8, I8Slot>;
   constexpr int RP = NTR * 16, KS = 2;
-  constexpr bool T_LDS = NTR > 0 && NTR <= 2;
+  constexpr bool T_LDS = !MX && NTR > 0 && NTR <= 2;
   constexpr int TROWB = RP * 4;  // bytes of one t row
-  __shared__ __attribute__((aligned(16))) I8Slot sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7;
+  constexpr int NDMA_STEP = MX ? 5 : 4;  // copies per DMA wave and step
+  __shared__ __attribute__((aligned(16))) Slot sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7;
   __shared__ __attribute__((aligned(16))) uint8_t t_tile[T_LDS ? 256 * TROWB : 16];
-  I8Slot* const ring[I4_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5, &sl6, &sl7};
+  Slot* const ring[I4_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5, &sl6, &sl7};
+  const float* const xs = static_cast<const float*>(xs_);
+  const float* const ws = static_cast<const float*>(ws_);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -144,7 +162,7 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, m_pad / I4_BM, n_pad / I4_BN, tm, tn);
   const int m0 = tm * I4_BM, n0 = tn * I4_BN;
-  const int S = K / 32;
+  const int S = MX ? K / W4A4_GROUP : K / 32;  // K steps of 32 bytes per row
 
   // DMA (waves 0..3 only): instruction q (0, 1) of wave w fills bytes [1024 (2w + q), + 1024) of
   // an operand's 8 KB, lane i the 16 bytes of row 32 (2w + q) + i / 2 that the swizzle puts there;
@@ -162,8 +180,16 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
   // Steps past the end fill their slot with zero codes: the lane offset is moved past the buffer's
   // range (a raw buffer load outside num_records returns zeros), so they add exactly 0 and the loop
   // needs no tail handling. The step offset goes in the scalar soffset, clamped to the last step.
-  auto dma = [&](int k, I8Slot* sl) {
-    const int v = c_lane | (k < S ? 0 : (int)0x80000000);
+  // MXFP4 block scales, E8M0 bytes [G][2][rows]: DMA wave w copies the 256 rows of block plane
+  // 2k + (w & 1) of A (w < 2) or B (w >= 2), 4 bytes per lane
+  const bool s_is_a = dw < 2;
+  const int s_rows = s_is_a ? m_pad : n_pad, s_row0 = s_is_a ? m0 : n0, s_plane = dw & 1;
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(s_is_a ? xs_ : ws_) + (MX ? s_row0 : 0)), 0,
+      MX ? 2 * S * s_rows - s_row0 : 0, RSRC_W3);
+  auto dma = [&](int k, Slot* sl) {
+    const int oob = k < S ? 0 : (int)0x80000000;
+    const int v = c_lane | oob;
     k = min(k, S - 1);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -172,6 +198,9 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr)(sl->b + 1024 * (2 * dw + q)), 16, v,
                                                k * n_pad * 32 + 1024 * q, 0, 0);
     }
+    if constexpr (MX)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr)(sl->s + 256 * dw), 4, (4 * lane) | oob,
+                                               (2 * k + s_plane) * s_rows, 0, 0);
   };
 
   constexpr int TCHUNK = T_LDS ? 256 * TROWB / W8_DMA_WAVES : 0;  // bytes of the t tile per DMA wave
@@ -189,7 +218,7 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
     // prologue: steps 0 .. NS-3 in flight; the t tile and step 0 landed
 #pragma unroll
     for (int k = 0; k < I4_NS - 2; ++k) dma(k, ring[k]);
-    wait_vmcnt<4 * (I4_NS - 3)>();
+    wait_vmcnt<NDMA_STEP * (I4_NS - 3)>();
   }
   __builtin_amdgcn_s_barrier();
 
@@ -197,13 +226,22 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
   const int arow0 = wm * 128 + lr, bcol0 = wn * 32 * W8_NT + lr;
   const int a_off = sw_off32(arow0, lh), b_off = sw_off32(bcol0, lh);
   // operands of step k + 1 are read during step k (double-buffered registers)
-  auto rd = [&](const I8Slot* sl, v4i (&A)[I4_MT], v4i (&B)[W8_NT]) {
+  // (MXFP4: and the E8M0 scale of each operand row for the lane's K block 2g + lh)
+  auto rd = [&](const Slot* sl, v4i (&A)[I4_MT], v4i (&B)[W8_NT], int (&sA)[I4_MT], int (&sB)[W8_NT]) {
 #pragma unroll
     for (int i = 0; i < I4_MT; ++i) A[i] = *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i);
 #pragma unroll
     for (int j = 0; j < W8_NT; ++j) B[j] = *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j);
+    if constexpr (MX) {
+      const uint8_t* sc = reinterpret_cast<const uint8_t*>(sl) + offsetof(MxSlot8, s);
+#pragma unroll
+      for (int i = 0; i < I4_MT; ++i) sA[i] = sc[256 * lh + arow0 + 32 * i];
+#pragma unroll
+      for (int j = 0; j < W8_NT; ++j) sB[j] = sc[512 + 256 * lh + bcol0 + 32 * j];
+    }
   };
-  v16i acc[I4_MT][W8_NT];
+  auto op8 = [](v4i v) { return v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0}; };
+  std::conditional_t<MX, v16f, v16i> acc[I4_MT][W8_NT];
 #pragma unroll
   for (int i = 0; i < I4_MT; ++i)
 #pragma unroll
@@ -211,41 +249,59 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
   v4i A[2][I4_MT], B[2][W8_NT];
-  rd(ring[0], A[0], B[0]);
+  int sA[2][I4_MT], sB[2][W8_NT];
+  rd(ring[0], A[0], B[0], sA[0], sB[0]);
   // The main loop, once for the DMA waves and once for the others (same barriers). Every step, a
   // DMA wave issues the copy of step k + NS - 2 into the slot of step k - 2 (free since the last
   // barrier); the LDS reads of the next step and these copies issue between the step's MFMAs.
   auto main_loop = [&](auto dma_tag) {
     constexpr bool D = decltype(dma_tag)::value;
-    constexpr int NMF = I4_MT * W8_NT, NRD = I4_MT + W8_NT, NDMA = D ? 4 : 0;
+    constexpr int NMF = I4_MT * W8_NT, NRD = I4_MT + W8_NT, NDMA = D ? NDMA_STEP : 0;
     for (int k0 = 0; k0 < S; k0 += I4_NS) {
 #pragma unroll
       for (int u = 0; u < I4_NS; ++u) {
         const int k = k0 + u, c = u & 1;
         if (u % 2 == 0) {
           // steps k+1 and k+2 have landed; everyone is done with slots k-2 and k-1
-          if (D) wait_vmcnt<4 * (I4_NS - 5)>();
+          if (D) wait_vmcnt<NDMA_STEP * (I4_NS - 5)>();
           __builtin_amdgcn_s_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
-        rd(ring[(u + 1) % I4_NS], A[c ^ 1], B[c ^ 1]);
+        rd(ring[(u + 1) % I4_NS], A[c ^ 1], B[c ^ 1], sA[c ^ 1], sB[c ^ 1]);
         if (D) dma(k + I4_NS - 2, ring[(u + I4_NS - 2) % I4_NS]);
 #pragma unroll
         for (int i = 0; i < I4_MT; ++i)
 #pragma unroll
-          for (int j = 0; j < W8_NT; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[c][i], B[c][j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < W8_NT; ++j) {
+            if constexpr (MX)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8(A[c][i]), op8(B[c][j]), acc[i][j], 4, 4, 0,
+                                                                        sA[c][i], 0, sB[c][j]);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[c][i], B[c][j], acc[i][j], 0, 0, 0);
+          }
+        if constexpr (MX) {  // 12 LDS reads (6 operands, 6 scale bytes) and 5 copies over 8 MFMAs
 #pragma unroll
-        for (int q = 0; q < NRD; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
+          for (int q = 0; q < 6; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (D) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // DMA loads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (D) __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);
+        } else {
 #pragma unroll
-        for (int q = 0; q < NDMA; ++q) {
-          if (NRD + q < NMF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA load
+          for (int q = 0; q < NRD; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          }
+#pragma unroll
+          for (int q = 0; q < NDMA; ++q) {
+            if (NRD + q < NMF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA load
+          }
+          if (NMF > NRD + NDMA) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD - NDMA, 0);
         }
-        if (NMF > NRD + NDMA) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD - NDMA, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -257,8 +313,15 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
   wait_vmcnt<0>();  // no LDS DMA may outlive the block
   __builtin_amdgcn_s_barrier();
 
-  // ---- epilogue: fp32 = int32 · (s_x[m] s_w[n]); then + bf16(t)·L2, + bias
+  // ---- epilogue: fp32 = int32 · (s_x[m] s_w[n]) (MXFP4: the accumulators as they are); then
+  // + bf16(t)·L2, + bias
   v16f out[I4_MT][W8_NT];
+  if constexpr (MX) {
+#pragma unroll
+    for (int i = 0; i < I4_MT; ++i)
+#pragma unroll
+      for (int j = 0; j < W8_NT; ++j) out[i][j] = acc[i][j];
+  } else {
   float swc[W8_NT];
 #pragma unroll
   for (int j = 0; j < W8_NT; ++j) swc[j] = ws[n0 + bcol0 + 32 * j];
@@ -276,6 +339,7 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
         const float sxv = (v & 3) == 0 ? q4.x : (v & 3) == 1 ? q4.y : (v & 3) == 2 ? q4.z : q4.w;
         out[i][j][v] = (float)acc[i][j][v] * (sxv * swc[j]);
       }
+  }
   }
   if constexpr (NTR > 0) {
 #pragma unroll
@@ -307,7 +371,7 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
 #pragma unroll
   for (int w = 1; w < W8_WAVES; ++w)
     if (wave == w) stage = reinterpret_cast<uint8_t*>(ring[w]);  // wave-uniform select
-  static_assert(64 * Y_ES <= (int)sizeof(I8Slot), "staging fits a ring slot");
+  static_assert(64 * Y_ES <= (int)sizeof(Slot), "staging fits a ring slot");
 #pragma unroll
   for (int hh = 0; hh < W8_NT / 2; ++hh) {  // the wave's columns as 64-column blocks
     v16f part[I4_MT][2];
@@ -320,12 +384,12 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
   }
 }
 
-template <int NTR>
-hipError_t launch_gemm_w8a8(const uint8_t* xq, const float* xs, const float* xl1, const uint8_t* wq, const float* ws,
+template <int NTR, bool MX = false>
+hipError_t launch_gemm_w8a8(const uint8_t* xq, const void* xs, const float* xl1, const uint8_t* wq, const void* ws,
                             const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy, int M, int N, int K,
                             int m_pad, int n_pad, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_w8a8_kernel<NTR>), dim3((m_pad / I4_BM) * (n_pad / I4_BN)), dim3(W8_THREADS), 0, st, xq,
-                     xs, xl1, wq, ws, l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
+  hipLaunchKernelGGL((gemm_w8a8_kernel<NTR, MX>), dim3((m_pad / I4_BM) * (n_pad / I4_BN)), dim3(W8_THREADS), 0, st,
+                     xq, xs, xl1, wq, ws, l2t, bias, Y, ldy, M, N, K, m_pad, n_pad);
   return hipGetLastError();
 }
 
@@ -351,6 +415,20 @@ hipError_t dispatch_gemm_w8a8(int ntr, const uint8_t* xq, const float* xscale, c
     W4A4_W8_CASE(0) W4A4_W8_CASE(1) W4A4_W8_CASE(2) W4A4_W8_CASE(3) W4A4_W8_CASE(4)
     W4A4_W8_CASE(5) W4A4_W8_CASE(6) W4A4_W8_CASE(7) W4A4_W8_CASE(8)
 #undef W4A4_W8_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_gemm_mx(int ntr, const uint8_t* xq, const uint8_t* xscale, const float* xl1, const uint8_t* wq,
+                            const uint8_t* wscale, const uint16_t* l2t, const uint16_t* bias, uint16_t* Y, int ldy,
+                            int M, int N, int K, int m_pad, int n_pad, hipStream_t st) {
+  switch (ntr) {
+#define W4A4_MX_CASE(n)                                                                                           \
+  case n:                                                                                                         \
+    return launch_gemm_w8a8<n, true>(xq, xscale, xl1, wq, wscale, l2t, bias, Y, ldy, M, N, K, m_pad, n_pad, st);
+    W4A4_MX_CASE(0) W4A4_MX_CASE(1) W4A4_MX_CASE(2) W4A4_MX_CASE(3) W4A4_MX_CASE(4)
+    W4A4_MX_CASE(5) W4A4_MX_CASE(6) W4A4_MX_CASE(7) W4A4_MX_CASE(8)
+#undef W4A4_MX_CASE
   }
   return hipErrorInvalidValue;
 }
