@@ -137,8 +137,10 @@ struct MxSlot8 {
 
 // MX = true: the same kernel on MXFP4 operands (FP4 E2M1 codes, 32 bytes per row and 64-group,
 // with E8M0 block scales applied by the scaled MFMA; fp32 accumulators, no scale epilogue). The
-// slots then also hold the step's block scales (one more copy per DMA wave and step), and t is
-// read from global memory in the epilogue, which keeps the LDS at 136 KB.
+// slots then also hold the step's block scales (one more copy per DMA wave and step), which leaves
+// no room for a t tile of its own: up to rank 32 the low-rank up projection runs before the main
+// loop with the t tile staged in the ring's last two slots, larger ranks add it in the epilogue
+// with t read from global memory.
 template <int NTR, bool MX = false>  // NTR = rank_pad / 16
 __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs_, const float* __restrict__ xl1,
@@ -203,9 +205,42 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
                                                (2 * k + s_plane) * s_rows, 0, 0);
   };
 
+  // MXFP4 with rank <= 32: the low-rank up projection goes first (the fp32 accumulators start at
+  // bf16(t)·L2 and the FP4 MFMAs accumulate on top). The block's t tile (256 rows x 32 fp32) is
+  // copied into ring slots 6 and 7, idle until the loop's first step, ahead of the ring copies, and
+  // the L2 operands are loaded into registers, so all of it lands under the prologue's wait.
+  constexpr bool MX_T = MX && NTR > 0 && NTR <= 2;
+  static_assert(!MX_T || 256 * TROWB <= 2 * 16384, "t tile fits slots 6 and 7");
+  v4i LBp[MX_T ? RP / 16 : 1][W8_NT];
+  if constexpr (MX_T) {
+#pragma unroll
+    for (int s2 = 0; s2 < RP / 16; ++s2)
+#pragma unroll
+      for (int j = 0; j < W8_NT; ++j)
+        LBp[s2][j] = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 32 * W8_NT + j * 32 + (lane & 31)) * RP +
+                                                   16 * s2 + 8 * (lane >> 5));
+  }
+  auto t_row_lds = [&](int r) -> const uint8_t* {  // row r of the t tile: first 16 KB in slot 6, rest in slot 7
+    const int byte = r * TROWB;
+    return byte < 16384 ? reinterpret_cast<const uint8_t*>(ring[6]) + byte
+                        : reinterpret_cast<const uint8_t*>(ring[7]) + (byte - 16384);
+  };
+
   constexpr int TCHUNK = T_LDS ? 256 * TROWB / W8_DMA_WAVES : 0;  // bytes of the t tile per DMA wave
   const bool dma_wave = wave < W8_DMA_WAVES;
   if (dma_wave) {
+    if constexpr (MX_T) {  // t tile -> slots 6 and 7, 1 KB per DMA instruction
+      const __amdgpu_buffer_rsrc_t t_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(xl1 + (size_t)m0 * RP), 0, (m_pad - m0) * TROWB, RSRC_W3);
+      constexpr int TCH = 256 * TROWB / W8_DMA_WAVES;
+#pragma unroll
+      for (int q = 0; q < TCH / 1024; ++q) {
+        const int off = dw * TCH + q * 1024;  // chunks never straddle the 16 KB split
+        uint8_t* dst = off < 16384 ? reinterpret_cast<uint8_t*>(ring[6]) + off
+                                   : reinterpret_cast<uint8_t*>(ring[7]) + (off - 16384);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr)dst, 16, 16 * lane, off, 0, 0);
+      }
+    }
     if (T_LDS) {  // t tile -> its LDS area, 1 KB per DMA instruction
       const __amdgpu_buffer_rsrc_t t_rsrc = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(xl1 + (size_t)m0 * RP), 0, (m_pad - m0) * TROWB, RSRC_W3);
@@ -257,6 +292,21 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
   auto main_loop = [&](auto dma_tag) {
     constexpr bool D = decltype(dma_tag)::value;
     constexpr int NMF = I4_MT * W8_NT, NRD = I4_MT + W8_NT, NDMA = D ? NDMA_STEP : 0;
+    if constexpr (MX_T) {  // acc = bf16(t)·L2 (32x32x16 bf16 MFMAs; t rows from LDS)
+#pragma unroll
+      for (int s2 = 0; s2 < RP / 16; ++s2)
+#pragma unroll
+        for (int i = 0; i < I4_MT; ++i) {
+          const float* tp = reinterpret_cast<const float*>(t_row_lds(wm * 128 + i * 32 + lr)) + 16 * s2 + 8 * lh;
+          const float4 t0 = *reinterpret_cast<const float4*>(tp), t1 = *reinterpret_cast<const float4*>(tp + 4);
+          const v4i TA = v4i{(int)pack_bf16x2(t0.x, t0.y), (int)pack_bf16x2(t0.z, t0.w), (int)pack_bf16x2(t1.x, t1.y),
+                             (int)pack_bf16x2(t1.z, t1.w)};
+#pragma unroll
+          for (int j = 0; j < W8_NT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(TA), as_bf16x8(LBp[s2][j]), acc[i][j], 0, 0, 0);
+        }
+    }
+
     for (int k0 = 0; k0 < S; k0 += I4_NS) {
 #pragma unroll
       for (int u = 0; u < I4_NS; ++u) {
@@ -341,7 +391,7 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
       }
   }
   }
-  if constexpr (NTR > 0) {
+  if constexpr (!MX_T && NTR > 0) {  // (MXFP4 ranks past 32: t and L2 straight from global memory)
 #pragma unroll
     for (int k0 = 0; k0 < RP; k0 += 32) {
 #pragma unroll
