@@ -325,6 +325,23 @@ def test_max_rank(fmt):
     check_y(g, O.linear(d["x"], inv, ref)["y"])
 
 
+@pytest.mark.parametrize("r", [48, 128])
+def test_mxfp4_large_grid_high_rank(r):
+    """MXFP4 on a grid too large for the 128 x 128 kernel (8 x 66 blocks of 128², so the INT8
+    GEMM's MXFP4 mode runs) with a rank above 32, whose up projection is added in the epilogue from
+    global memory instead of before the main loop; ragged M and N, canary columns past N."""
+    m, k, n = 1000, 256, 8440
+    d = synth.make_layer(m, k, n, n_outliers=4, outlier_scale=30.0, seed=r)
+    lam, inv = _smooth(d)
+    ref = oracle_weights(d, r, "mxfp4_b32", lam)
+    print(f"[mxfp4 large grid] M={m} K={k} N={n} r={r}", flush=True)
+    g = gpu_layer(d, lam, inv, r, "mxfp4_b32", ref, pad_cols=3)
+    check_activation_side(d, inv, ref, "mxfp4_b32", g)
+    rows = _sample_rows(m, n=40, seed=r)
+    check_y(g, O.linear(d["x"][rows], inv, ref)["y"], rows)
+    assert np.all(g["y"][:, n:] == -7.0), "wrote outside the M x N block"
+
+
 def test_w8a8_largest_k():
     """W8A8 at the largest K whose int32 dot products cannot overflow (127² · 131072 < 2^31), with
     rows of near-full-scale codes so that the exact sums come close to the limit."""
