@@ -395,7 +395,17 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(s_buf + s_first), 0, s_total - s_first, RSRC_W3);
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  // 3 vector-memory instructions per wave and group; groups past the end reload the last group
+  // 3 vector-memory instructions per wave and group (part 0: A codes, 1: B codes, 2: scales);
+  // groups past the end reload the last group
+  auto dma_part = [&](int part, int g, I4Slot* sl) {
+    g = min(g, G - 1);
+    if (part == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr)(sl->a + 1024 * wave), 16, c_lane, g * m_pad * 32, 0, 0);
+    else if (part == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr)(sl->b + 1024 * wave), 16, c_lane, g * n_pad * 32, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr)(sl->s + 128 * sblk), 4, s_lane, g * s_gstride, 0, 0);
+  };
   auto dma = [&](int g, I4Slot* sl) {
     g = min(g, G - 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr)(sl->a + 1024 * wave), 16, c_lane, g * m_pad * 32, 0, 0);
@@ -597,11 +607,10 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
       const I4Slot* nxt = ring[(u + 1) % I4_NS];
       if (u % 2 == 0) {
         // groups g+1 and g+2 have landed in every wave's share of their slots; everyone is done
-        // with slots g-2 and g-1, which take groups g+NS-2 and g+NS-1
+        // with slots g-2 and g-1, which take groups g+NS-2 (copied during this group) and g+NS-1
+        // (during the next)
         wait_vmcnt<3 * (I4_NS - 5)>();
         __builtin_amdgcn_s_barrier();
-        dma(g + I4_NS - 2, ring[(u + I4_NS - 2) % I4_NS]);
-        dma(g + I4_NS - 1, ring[(u + I4_NS - 1) % I4_NS]);
       }
       const bool live1 = g + 1 < G;
       // ---- the group's 8 tiles, software-pipelined: the FP6 MFMA of tile t+1 is issued before the
@@ -642,6 +651,10 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
             OBn[jj] = sb_val(nxt, jj, live1);
           }
         }
+        // this group's copy of group g + NS - 2 into the slot freed at the last barrier, one
+        // instruction every other tile (issued together right after the barrier, the copies of all
+        // eight waves queue up at once and stall their issue: measured 5-7% slower)
+        if (t == 1 || t == 3 || t == 5) dma_part(t >> 1, g + I4_NS - 2, ring[(u + I4_NS - 2) % I4_NS]);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch reads here, two tiles ahead of their use
         // raised wave priority around each MFMA issue keeps the matrix pipe fed while the other
         // wave of the SIMD is in its FMAs
@@ -954,25 +967,26 @@ __global__ __launch_bounds__(MX_THREADS, 2) void gemm_mx_small_kernel(
     for (int u = 0; u < MX_NS; ++u) {
       const int g = g0 + u, c = u & 1;
       if (u % 2 == 0) {
-        // groups g+1 and g+2 have landed; everyone is done with slots g-2 and g-1
+        // groups g+1 and g+2 have landed; everyone is done with slots g-2 and g-1, which take
+        // groups g+NS-2 (copied during this group) and g+NS-1 (during the next)
         wait_vmcnt<3 * (MX_NS - 5)>();
         __builtin_amdgcn_s_barrier();
-        dma(g + MX_NS - 2, ring[(u + MX_NS - 2) % MX_NS]);
-        dma(g + MX_NS - 1, ring[(u + MX_NS - 1) % MX_NS]);
       }
       __builtin_amdgcn_sched_barrier(0);
       rd(ring[(u + 1) % MX_NS], A[c ^ 1], B[c ^ 1], sA[c ^ 1], sB[c ^ 1]);
+      dma(g + MX_NS - 2, ring[(u + MX_NS - 2) % MX_NS]);
 #pragma unroll
       for (int t = 0; t < 2 * MX_MT; ++t) {
         const int i = t >> 1, j = t & 1;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8(A[c][i]), op8(B[c][j]), acc[i][j], 4, 4, 0,
                                                                   sA[c][i], 0, sB[c][j]);
       }
-      // the next group's LDS reads issue between this group's MFMAs
+      // the next group's LDS reads and this group's copies issue between this group's MFMAs
 #pragma unroll
       for (int q = 0; q < 2 * MX_MT; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+        if (q < 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // the rest of the reads
       __builtin_amdgcn_sched_barrier(0);
