@@ -25,8 +25,14 @@
  *  - Errors: every argument is validated on the host before anything is launched or written;
  *    a failed check returns a status and leaves outputs untouched. Device calls return
  *    W4A4_ERR_HIP if a launch fails; faults inside kernels surface at the caller's stream
- *    synchronization. No C++ exception crosses the ABI.
- *  - Inputs are assumed finite. Device pointers must be 16-byte aligned.
+ *    synchronization. No C++ exception crosses the ABI (host memory exhaustion returns
+ *    W4A4_ERR_HOST_MEMORY).
+ *  - Non-finite values: the host calls scan their bf16 / fp32 inputs (weights, given factors,
+ *    channel maxima, LoRA factors) and return W4A4_ERR_NUMERIC, writing nothing, if one is Inf or
+ *    NaN. The device calls do not scan activations: a non-finite activation gives unspecified codes,
+ *    scales and outputs in its row (other rows are unaffected); it never makes a kernel read or
+ *    write out of bounds.
+ *  - Device pointers must be 16-byte aligned.
  */
 #ifndef W4A4_H
 #define W4A4_H
@@ -50,8 +56,9 @@ typedef enum {
   W4A4_OK = 0,
   W4A4_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment, rank out of range ... */
   W4A4_ERR_UNSUPPORTED = 2,  /* unknown format */
-  W4A4_ERR_NUMERIC = 3,      /* non-finite / non-normal smoothing factor, SVD failure */
-  W4A4_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+  W4A4_ERR_NUMERIC = 3,      /* non-finite input, non-normal smoothing factor, SVD failure */
+  W4A4_ERR_HIP = 4,          /* a HIP launch or runtime call failed */
+  W4A4_ERR_HOST_MEMORY = 5   /* a host-side allocation failed */
 } w4a4_status_t;
 
 typedef enum {
@@ -107,7 +114,8 @@ w4a4_status_t w4a4_buffer_sizes(int M, int N, int K, int rank, int fmt, w4a4_siz
 
 /*
  * out[j] = max_i |A[i, j]| for a bf16 matrix A [rows][lda] (the activation / weight channel
- * maxima the smoothing factor is built from, App. D). Thread-safe.
+ * maxima the smoothing factor is built from, App. D). Thread-safe. W4A4_ERR_NUMERIC (out not
+ * written) if A holds an Inf or NaN.
  */
 w4a4_status_t w4a4_column_absmax(const uint16_t* A, int rows, int cols, int lda, float* out);
 
@@ -115,8 +123,9 @@ w4a4_status_t w4a4_column_absmax(const uint16_t* A, int rows, int cols, int lda,
  * Smoothing factors (App. D, after SmoothQuant): λ_j = max|X_j|^α / max|W_j|^(1-α).
  * α = 0.5 is computed as fp32(sqrt(double(ax)/double(aw))); other α in (0, 1) as
  * fp32(pow(ax, α) / pow(aw, 1 - α)) in double. λ_j = 1 when ax or aw is 0.
- * inv_lambda[j] = 1.0f / λ_j (IEEE float division). W4A4_ERR_NUMERIC if a λ_j is not a
- * finite normal float; W4A4_ERR_INVALID_ARG for α outside (0, 1) or negative maxima.
+ * inv_lambda[j] = 1.0f / λ_j (IEEE float division). W4A4_ERR_NUMERIC if a maximum is not finite
+ * or a λ_j is not a finite normal float; W4A4_ERR_INVALID_ARG for α outside (0, 1) or negative
+ * maxima. Nothing is written on error.
  */
 w4a4_status_t w4a4_smooth_factors(const float* amax_x, const float* amax_w, int K, float alpha,
                                   float* lambda, float* inv_lambda);
@@ -133,7 +142,9 @@ w4a4_status_t w4a4_smooth_factors(const float* amax_x, const float* amax_w, int 
  *          (randomized subspace iteration + one-sided Jacobi; deterministic).
  *   wq, wscale, l1t, l2t  host outputs sized by w4a4_buffer_sizes (copy them to the device).
  *   L1_out [K][rank], L2_out [rank][N] bf16 (host, optional, may be NULL): the factors used.
- * Thread-safe; uses several CPU threads.
+ * Thread-safe; uses several CPU threads. W4A4_ERR_NUMERIC if W (or a given factor) holds an Inf
+ * or NaN, or the SVD does not converge; W4A4_ERR_INVALID_ARG for a λ_j that is not a positive finite
+ * float.
  */
 w4a4_status_t w4a4_prepare_weights(const uint16_t* W, int N, int K, const float* lambda, int rank,
                                    int fmt, const uint16_t* L1_in, const uint16_t* L2_in,

@@ -329,3 +329,120 @@ def test_mlp_pair_entry_points_validate_before_launch():
     assert w4.gelu_quant_xl1_bytes(300, 640, 20) == 512 * 32 * 4 * (1 + 3)
     assert w4.gelu_quant_xl1_bytes(300, 256, 20) == 512 * 32 * 4
     assert w4.gelu_quant_xl1_bytes(300, 256, 0) == 0
+
+
+def test_binding_validates_tensors_before_the_library():
+    """The Python binding rejects tensors whose dtype, layout, shape, size or device would make a
+    kernel read or write out of bounds; none of these calls reaches libw4a4."""
+    import torch
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    M, K, N, r = 300, 256, 320, 16
+    sz = w4.buffer_sizes(M, N, K, r)
+    cpu = torch.device("cpu")
+    buf = lambda n, dt=u8: torch.zeros(max(n, 16) // torch.tensor([], dtype=dt).element_size(), dtype=dt)
+    xq, xs, xl1 = buf(sz["xq"]), buf(sz["xscale"]), buf(sz["xl1"], f32)
+    wq, ws, l1t, l2t = buf(sz["wq"]), buf(sz["wscale"]), buf(sz["l1t"], torch.int16), buf(sz["l2t"], torch.int16)
+    inv = buf(4 * K, f32)
+    x = torch.zeros((M, K), dtype=bf)
+    y = torch.zeros((M, N), dtype=bf)
+    with pytest.raises(ValueError, match="bfloat16"):
+        w4.quantize_act(x.float(), inv, l1t, r, 0, xq, xs, xl1)
+    with pytest.raises(ValueError, match="unit stride"):
+        w4.quantize_act(torch.zeros((K, M), dtype=bf).t(), inv, l1t, r, 0, xq, xs, xl1)
+    with pytest.raises(ValueError, match="GPU"):                       # a host tensor
+        w4.quantize_act(x, inv, l1t, r, 0, xq, xs, xl1)
+    with pytest.raises(ValueError, match="needs at least"):            # Y with too few rows
+        w4.lowrank_linear(xq, xs, xl1, wq, ws, l2t, None, y[: M - 1], M, N, K, r, 0)
+    with pytest.raises(ValueError, match="needs at least"):            # Y with too few columns
+        w4.lowrank_linear(xq, xs, xl1, wq, ws, l2t, None, y[:, : N - 1], M, N, K, r, 0)
+    with pytest.raises(ValueError, match="bytes, needs"):              # weight codes sized for a smaller N
+        w4.lowrank_linear(xq, xs, xl1, wq[: sz["wq"] // 2], ws, l2t, None, y, M, N, K, r, 0)
+    with pytest.raises(ValueError, match="bytes, needs"):              # bias shorter than N
+        w4.lowrank_linear(xq, xs, xl1, wq, ws, l2t, buf(2 * N - 2, torch.int16), y, M, N, K, r, 0)
+    with pytest.raises(ValueError, match="contiguous"):
+        w4.lowrank_linear(xq, xs, xl1, wq, ws, l2t.view(-1, 2).t(), None, y, M, N, K, r, 0)
+    with pytest.raises(TypeError):
+        w4.lowrank_linear(xq, xs, xl1, None, ws, l2t, None, y, M, N, K, r, 0)
+    # a layer object checks x against its K before anything else
+    layer = object.__new__(w4.W4A4Linear)
+    layer.K, layer.device = K, cpu
+    with pytest.raises(ValueError, match="needs \\[M, 256\\]"):
+        layer.quantize(torch.zeros((M, K + 64), dtype=bf))
+
+
+def test_non_finite_inputs_are_rejected():
+    """Inf / NaN in any host input gives W4A4_ERR_NUMERIC and leaves the outputs untouched."""
+    L = w4.lib()
+    p = lambda a: ctypes.c_void_p(a.ctypes.data)
+    rng = np.random.default_rng(9)
+    N, K = 8, 64
+    w = synth.f32_to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32))
+    lam = np.ones(K, np.float32)
+    sz = w4.buffer_sizes(1, N, K, 0)
+    for bad in (0x7F80, 0xFF80, 0x7FC1):            # +Inf, -Inf, NaN (bf16 bit patterns)
+        wb = w.copy()
+        wb[3, 17] = bad
+        out = np.full(K, -1.0, np.float32)
+        assert L.w4a4_column_absmax(p(wb), N, K, K, p(out)) == 3
+        assert np.all(out == -1.0)
+        wq = np.full(sz["wq"], 0xAB, np.uint8)
+        ws = np.full(sz["wscale"], 0xAB, np.uint8)
+        assert L.w4a4_prepare_weights(p(wb), N, K, p(lam), 0, 0, None, None, p(wq), p(ws),
+                                      None, None, None, None) == 3
+        assert np.all(wq == 0xAB) and np.all(ws == 0xAB)
+    # a non-finite channel maximum
+    ax = np.ones(K, np.float32)
+    lo, io = np.zeros(K, np.float32), np.zeros(K, np.float32)
+    for v in (np.inf, np.nan):
+        a2 = ax.copy()
+        a2[5] = v
+        assert L.w4a4_smooth_factors(p(a2), p(ax), K, ctypes.c_float(0.5), p(lo), p(io)) == 3
+        assert L.w4a4_smooth_factors(p(ax), p(a2), K, ctypes.c_float(0.5), p(lo), p(io)) == 3
+        assert not lo.any() and not io.any()
+    # non-finite factors given to the preparation, or to the LoRA merge
+    r = 2
+    l1 = synth.f32_to_bf16_bits(rng.standard_normal((K, r)).astype(np.float32))
+    l2 = synth.f32_to_bf16_bits(rng.standard_normal((r, N)).astype(np.float32))
+    l1[7, 1] = 0x7FC0
+    s2 = w4.buffer_sizes(1, N, K, r)
+    bufs = [np.zeros(s2[k], np.uint8) for k in ("wq", "wscale", "l1t", "l2t")]
+    assert L.w4a4_prepare_weights(p(w), N, K, p(lam), r, 0, p(l1), p(l2), *[p(b) for b in bufs], None, None) == 3
+    l1t = np.zeros(s2["l1t"] // 2, np.uint16)
+    l2t = np.zeros(s2["l2t"] // 2, np.uint16)
+    so = w4.buffer_sizes(1, N, K, 2 * r)
+    o1, o2 = np.zeros(so["l1t"] // 2, np.uint16), np.zeros(so["l2t"] // 2, np.uint16)
+    assert L.w4a4_append_lowrank(p(l1t), p(l2t), K, N, r, p(l1), p(l2), r, p(o1), p(o2)) == 3
+    assert w4.lib().w4a4_status_str(5) == b"host memory allocation failed"
+
+
+def test_shape_checks_do_not_overflow():
+    """Row counts close to INT_MAX are rejected instead of wrapping when padded to 256."""
+    s = w4._Sizes()
+    big = 2 ** 31 - 1
+    assert w4.lib().w4a4_buffer_sizes(big, 64, 64, 0, 0, ctypes.byref(s)) == 1
+    assert w4.lib().w4a4_buffer_sizes(64, big - 100, 64, 0, 0, ctypes.byref(s)) == 1
+
+
+def test_host_half_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """The host half (w4a4_host.cpp, plain C++) built with ASan + UBSan and driven through its C ABI by
+    a small program (tests/host_sanitize_main.cpp): the preparations, refinement, LoRA merge, canonical
+    layouts and argument checks run clean (any report aborts the program)."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "host_sanitize")
+    src = os.path.join(ROOT, "w4a4_quantized_gemm_smooth_amd", "csrc", "w4a4_host.cpp")
+    drv = os.path.join(ROOT, "tests", "host_sanitize_main.cpp")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-pthread",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "w4a4_quantized_gemm_smooth_amd", "csrc"),
+           src, drv, "-o", exe]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    run = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=600)
+    assert run.returncode == 0, (run.stdout[-2000:], run.stderr[-4000:])
+    assert "host half OK" in run.stdout

@@ -173,6 +173,60 @@ def test_pack_int4_layout():
     assert O.pack_int4(q).tolist() == [[0xF1, 0x78, 0x87, 0xD0]]
 
 
+def test_pack_nibbles_golden():
+    """Golden bytes of the canonical MXFP4 packing: E2M1 fields unchanged, element 2i in the low
+    nibble (negative zero 0x8 and the sign bit of every field survive, no sign extension)."""
+    cases, cur = [], None
+    import os
+    from conftest import GOLDEN
+    for line in open(os.path.join(GOLDEN, "pack_nibbles_cases.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *vals = line.split()
+        if key == "case":
+            cur = {"codes": [int(v, 16) for v in vals]}
+            cases.append(cur)
+        else:
+            cur["bytes"] = [int(v, 16) for v in vals]
+    assert len(cases) == 3
+    for c in cases:
+        got = O.pack_nibbles(np.array([c["codes"]], dtype=np.uint8))
+        assert got.tolist() == [c["bytes"]], c
+        # two rows at once: rows are packed independently
+        two = O.pack_nibbles(np.array([c["codes"], c["codes"][::-1]], dtype=np.uint8))
+        assert two[0].tolist() == c["bytes"]
+
+
+def test_linear_bias_hand_worked():
+    """A 1 x 64 layer worked by hand: λ = 1, rank 0, x = (7, 0, ..., 0) gives s_x = bf16(7/7) = 1 and
+    q_x = (7, 0, ...); weight row 0 = (0.875, 0, ...) gives s_w = 0.125, q_w = 7; row 1 = (-1.75, 0, ...)
+    gives s_w = 0.25, q_w = -7; so Y_main = (1·0.125·49, 1·0.25·(-49)) = (6.125, -12.25). The bias
+    is added before the single rounding to bf16 (step 2^-5 at 6.125, 2^-4 at 12.25):
+      bias (0.5, -0.75)               -> (6.625, -13.0)      exact
+      bias (2^-6, 2^-5)               -> (6.125, -12.25)     6.140625 is a tie -> even 6.125;
+                                                             -12.21875 is a tie -> even -12.25
+      bias (2^-6 + 2^-10, -2^-5 - 2^-9) -> (6.15625, -12.3125)  just past the ties, rounded away
+      no bias                         -> (6.125, -12.25)"""
+    x = np.zeros((1, 64), np.float32)
+    x[0, 0] = 7.0
+    w = np.zeros((2, 64), np.float32)
+    w[0, 0], w[1, 0] = 0.875, -1.75
+    lam = np.ones(64, np.float32)
+    prep = O.prepare_weights(O.f32_to_bf16_bits(w), lam, 0)
+    assert prep["sw"].tolist() == [[0.125], [0.25]] and prep["cw"][:, 0].tolist() == [7, -7]
+    xb = O.f32_to_bf16_bits(x)
+    cases = [((0.5, -0.75), (6.625, -13.0)),
+             ((2.0 ** -6, 2.0 ** -5), (6.125, -12.25)),
+             ((2.0 ** -6 + 2.0 ** -10, -2.0 ** -5 - 2.0 ** -9), (6.15625, -12.3125))]
+    for bias, want in cases:
+        b = O.f32_to_bf16_bits(np.array(bias, np.float32))
+        assert O.bf16_bits_to_f32(b).tolist() == list(bias)          # the biases are bf16 values
+        y = O.linear(xb, lam, prep, b)["y"]
+        assert y[0].tolist() == list(want), (bias, y)
+    assert O.linear(xb, lam, prep)["y"][0].tolist() == [6.125, -12.25]
+
+
 # ---------------------------------------------------------------- FP4 (E2M1) block quantizer
 def _block(values):
     b = np.zeros((1, 32), dtype=np.float32)
@@ -420,20 +474,33 @@ def test_prop41_bound():
 
 
 # ---------------------------------------------------------------- exact end-to-end case
+def _force_full_scale(q, rng, block, val):
+    """Put +val into one element and -val into another of every block of each row, so that every
+    block's maximum magnitude is val (the scale is then exactly its power-of-two factor)."""
+    rows, k = q.shape
+    for b in range(k // block):
+        pos = rng.permutation(block)[:2]
+        q[:, b * block + pos[0]] = val
+        q[:, b * block + pos[1]] = -val
+    return q
+
+
 def exact_case(m=64, k=128, n=96, r=2, seed=3):
-    """A layer on which every rounding in the method is exact (λ = 1, power-of-two scales,
-    representable activations and residual, one-hot L1). Returns inputs and the exact Y (Fractions)."""
+    """A layer on which every rounding in the method is exact (λ = 1, power-of-two group scales,
+    representable activations and residual, one-hot L1). Returns inputs and the exact Y.
+
+    Every group of every row holds a code of +7 and one of -7, so each INT4 scale is exactly
+    7·2^e / 7 = 2^e. Exactness of any fp32 summation order: x·8 and resid·64 are integers bounded by
+    7·4·8 and 7·2^-4·64, so every partial sum of x·resid is a multiple of 2^-9 below K·6272·2^-9 in
+    magnitude; the bound is asserted below 2^24 units (fp32-exact) and, with it, below 2^53 (the fp64
+    matmul used here is exact too)."""
     rng = np.random.default_rng(seed)
     g = k // 64
     ex = rng.integers(-3, 3, size=(m, g))
-    qx = rng.integers(-7, 8, size=(m, k))
-    qx[np.arange(m), rng.integers(0, 64, size=m)] = 7
-    qx[:, 64:][np.arange(m), rng.integers(0, 64, size=m)] = -7
+    qx = _force_full_scale(rng.integers(-7, 8, size=(m, k)), rng, 64, 7)
     x = qx * np.repeat(2.0 ** ex, 64, axis=1)
     ew = rng.integers(-6, -3, size=(n, g))
-    qw = rng.integers(-7, 8, size=(n, k))
-    qw[np.arange(n), rng.integers(0, 64, size=n)] = 7
-    qw[:, 64:][np.arange(n), rng.integers(0, 64, size=n)] = -7
+    qw = _force_full_scale(rng.integers(-7, 8, size=(n, k)), rng, 64, 7)
     resid = qw * np.repeat(2.0 ** ew, 64, axis=1)
     sel = rng.choice(k, r, replace=False)
     l1 = np.zeros((k, r))
@@ -442,14 +509,47 @@ def exact_case(m=64, k=128, n=96, r=2, seed=3):
     w = resid + (l1 @ l2).T
     bits = lambda a: O.f32_to_bf16_bits(a.astype(np.float32))
     assert np.array_equal(O.bf16_bits_to_f32(bits(x)), x) and np.array_equal(O.bf16_bits_to_f32(bits(w)), w)
-    # exact result in scaled integers: x*2^3, resid*2^6 and l2*2^3 are integers (int64 matmul is exact)
-    xi = (x * 8).astype(np.int64)
-    ri = (resid * 64).astype(np.int64)
-    li = (l2 * 8).astype(np.int64)
-    acc = xi @ ri.T + 8 * (xi[:, sel] @ li)
-    y = acc.astype(np.float64) / 512.0
-    assert np.all(np.abs(acc) < 2 ** 53)
+    # exact result in scaled integers: x*2^3, resid*2^6 and l2*2^3 are integers
+    assert k * (7 * 4 * 8) * (7 * 64 // 16) + r * 8 * (7 * 4 * 8) * 3 < 2 ** 24
+    xi = x * 8
+    ri = resid * 64
+    li = l2 * 8
+    acc = xi @ ri.T + 8 * (xi[:, sel] @ li)       # integer-valued fp64, exact below 2^53
+    y = acc / 512.0
     # cross-check a few entries with rational arithmetic
+    for i, j in ((0, 0), (m - 1, n - 1), (m // 2, n // 3)):
+        fr = sum(Fraction(float(x[i, kk])) * Fraction(float(resid[j, kk])) for kk in range(k)) + \
+            sum(Fraction(float(x[i, sel[t]])) * Fraction(float(l2[t, j])) for t in range(r))
+        assert Fraction(float(y[i, j])) == fr
+    return dict(x_bits=bits(x), w_bits=bits(w), l1=l1.astype(np.float32), l2=l2.astype(np.float32),
+                y_exact=y, rank=r)
+
+
+def mx_exact_case(m=64, k=128, n=96, r=2, seed=5):
+    """The MXFP4 counterpart of ``exact_case``: activations and residual are E2M1 values times a
+    power of two per 32-block, with a ±6 in every block (so the block exponent is exactly that power),
+    λ = 1 and a one-hot L1. Products of two E2M1 values are multiples of 1/4; with block exponents
+    ex in [-3, 0] and ew in [-6, -4] every partial sum is a multiple of 2^-11 bounded by
+    K·36·2^-4 (+ the low-rank terms), asserted below 2^24 units, so fp32 accumulation in any order is
+    exact and Y must be reproduced bit for bit."""
+    rng = np.random.default_rng(seed)
+    b = k // 32
+    grid = np.concatenate([O.E2M1_GRID, -O.E2M1_GRID[1:]])            # no negative zero
+    vx = _force_full_scale(rng.choice(grid, size=(m, k)), rng, 32, 6.0)
+    vw = _force_full_scale(rng.choice(grid, size=(n, k)), rng, 32, 6.0)
+    ex = rng.integers(-3, 1, size=(m, b))
+    ew = rng.integers(-6, -3, size=(n, b))
+    x = vx * np.repeat(2.0 ** ex, 32, axis=1)
+    resid = vw * np.repeat(2.0 ** ew, 32, axis=1)
+    sel = rng.choice(k, r, replace=False)
+    l1 = np.zeros((k, r))
+    l1[sel, np.arange(r)] = 1.0
+    l2 = rng.integers(-3, 4, size=(r, n)) * 0.125
+    w = resid + (l1 @ l2).T
+    bits = lambda a: O.f32_to_bf16_bits(a.astype(np.float32))
+    assert np.array_equal(O.bf16_bits_to_f32(bits(x)), x) and np.array_equal(O.bf16_bits_to_f32(bits(w)), w)
+    assert (k * 36 * 2.0 ** -4 + r * 6 * 0.375) * 2 ** 11 < 2 ** 24
+    y = x @ resid.T + x[:, sel] @ l2                   # dyadic, exact in fp64
     for i, j in ((0, 0), (m - 1, n - 1), (m // 2, n // 3)):
         fr = sum(Fraction(float(x[i, kk])) * Fraction(float(resid[j, kk])) for kk in range(k)) + \
             sum(Fraction(float(x[i, sel[t]])) * Fraction(float(l2[t, j])) for t in range(r))
@@ -465,6 +565,21 @@ def test_exact_case_end_to_end():
     out = O.linear(c["x_bits"], lam, prep)
     assert np.array_equal(out["y_m"] + out["y_l"], c["y_exact"])
     assert np.array_equal(out["y"], O.bf16_rne(c["y_exact"].astype(np.float32)))
+    # every group's scale is the exact power of two, and the codes are the constructed integers
+    assert np.all(np.log2(out["sx"][out["sx"] > 0]) % 1 == 0)
+    assert np.abs(out["cx"]).max() == 7 and np.abs(prep["cw"]).max() == 7
+
+
+def test_mx_exact_case_end_to_end():
+    c = mx_exact_case(m=40, k=160, n=72, r=3)
+    lam = np.ones(160, np.float32)
+    prep = O.prepare_weights(c["w_bits"], lam, c["rank"], "mxfp4_b32", l1=c["l1"], l2=c["l2"])
+    out = O.linear(c["x_bits"], lam, prep)
+    assert np.array_equal(out["y_m"] + out["y_l"], c["y_exact"])
+    assert np.array_equal(out["y"], O.bf16_rne(c["y_exact"].astype(np.float32)))
+    # decoded codes times 2^e give back the constructed values: the block exponent was chosen exactly
+    assert np.array_equal(O.dequant_mxfp4_b32(out["cx"], out["sx"]), O.bf16_bits_to_f32(c["x_bits"]))
+    assert np.array_equal(O.dequant_mxfp4_b32(prep["cw"], prep["sw"]), prep["r"])
 
 
 # ---------------------------------------------------------------- LoRA merge (§4.2 / §5.2)

@@ -225,16 +225,80 @@ def _dptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_matrix(name, t, rows, cols, device=None):
+    """A bf16 matrix the kernels read or write by rows: 2-D, unit stride along a row, at least
+    ``rows`` x ``cols`` (the kernels address row i at i * stride(0)), on ``device`` if given."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16 (got {t.dtype})")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit stride along its last dimension")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} is {tuple(t.shape)}, needs at least ({rows}, {cols})")
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on {device or 'a GPU'} (got {t.device})")
+
+
+def _check_buffer(name, t, nbytes, device):
+    """A library-layout device buffer of at least ``nbytes`` bytes (None allowed when 0 are needed)."""
+    import torch
+    if nbytes == 0 and t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor of {nbytes} bytes")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _check_activation_args(x, inv_lambda, l1t, rank, fmt, xq, xscale, xl1):
+    """Shapes, dtypes, devices and sizes of an activation-side call, checked before the launch."""
+    M, K = x.shape if hasattr(x, "shape") and len(x.shape) == 2 else (0, 0)
+    _check_matrix("x", x, M, K)
+    dev = x.device
+    sz = buffer_sizes(M, max(rank, 1), K, rank, fmt)
+    _check_buffer("inv_lambda", inv_lambda, 4 * K, dev)
+    _check_buffer("l1t", l1t, sz["l1t"], dev)
+    _check_buffer("xq", xq, sz["xq"], dev)
+    _check_buffer("xscale", xscale, sz["xscale"], dev)
+    _check_buffer("xl1", xl1, sz["xl1"], dev)
+
+
+def _check_gemm_args(xq, xscale, xl1, wq, wscale, l2t, bias, y, M, N, K, rank, fmt):
+    """Shapes, dtypes, devices and sizes of a GEMM call, checked before the launch."""
+    import torch
+    if not isinstance(xq, torch.Tensor):
+        raise TypeError("xq must be a torch tensor")
+    dev = xq.device
+    sz = buffer_sizes(M, N, K, rank, fmt)
+    # the GEMM reads the scales and t only, not the activation kernel's scratch behind them
+    xs_bytes = sz["m_pad"] * 4 if _fmt(fmt) == FMT_W8A8 else sz["xscale"]
+    t_bytes = sz["m_pad"] * sz["rank_pad"] * 4
+    for name, t, n in (("xq", xq, sz["xq"]), ("xscale", xscale, xs_bytes), ("xl1", xl1, t_bytes),
+                       ("wq", wq, sz["wq"]), ("wscale", wscale, sz["wscale"]), ("l2t", l2t, sz["l2t"])):
+        _check_buffer(name, t, n, dev)
+    if bias is not None:
+        _check_buffer("bias", bias, 2 * N, dev)
+    if y is not None:
+        _check_matrix("y", y, M, N, dev)
+
+
 def quantize_act(x, inv_lambda, l1t, rank, fmt, xq, xscale, xl1, stream=None):
     """Launch the activation kernel on `stream` (torch stream; default: current). x: [M, K] bf16
     (row stride x.stride(0)); other tensors are library-layout device buffers."""
     M, K = x.shape
+    _check_activation_args(x, inv_lambda, l1t, rank, fmt, xq, xscale, xl1)
     _check("w4a4_quantize_act", lib().w4a4_quantize_act(
         _dptr(x), M, K, x.stride(0), _dptr(inv_lambda), _dptr(l1t), rank, _fmt(fmt), _dptr(xq), _dptr(xscale),
         _dptr(xl1), _stream(stream)))
@@ -242,6 +306,7 @@ def quantize_act(x, inv_lambda, l1t, rank, fmt, xq, xscale, xl1, stream=None):
 
 def lowrank_linear(xq, xscale, xl1, wq, wscale, l2t, bias, y, M, N, K, rank, fmt, stream=None):
     """Launch the fused 4-bit GEMM + low-rank epilogue; y: [M, >=N] bf16 (row stride y.stride(0))."""
+    _check_gemm_args(xq, xscale, xl1, wq, wscale, l2t, bias, y, M, N, K, rank, fmt)
     _check("w4a4_lowrank_linear", lib().w4a4_lowrank_linear(
         _dptr(xq), _dptr(xscale), _dptr(xl1), _dptr(wq), _dptr(wscale), _dptr(l2t), _dptr(bias), _dptr(y),
         y.stride(0), M, N, K, rank, _fmt(fmt), _stream(stream)))
@@ -250,6 +315,7 @@ def lowrank_linear(xq, xscale, xl1, wq, wscale, l2t, bias, y, M, N, K, rank, fmt
 def gelu_quantize_act(y, inv_lambda, l1t, rank, fmt, xq, xscale, xl1, stream=None):
     """The activation kernel on X = bf16(GELU(y)) of a producer's bf16 output y [M, K] (INT4)."""
     M, K = y.shape
+    _check_activation_args(y, inv_lambda, l1t, rank, fmt, xq, xscale, xl1)
     _check("w4a4_gelu_quantize_act", lib().w4a4_gelu_quantize_act(
         _dptr(y), M, K, y.stride(0), _dptr(inv_lambda), _dptr(l1t), rank, _fmt(fmt), _dptr(xq), _dptr(xscale),
         _dptr(xl1), _stream(stream)))
@@ -259,6 +325,14 @@ def lowrank_linear_gelu_quant(xq, xscale, xl1, wq, wscale, l2t, bias, M, N, K, r
                               xq2, xscale2, xl1_2, y=None, stream=None):
     """fc1's GEMM with fc2's activation side (GELU, smoothing, INT4 codes, t2) in its epilogue;
     y (optional, [M, >=N] bf16) receives fc1's output for checking."""
+    _check_gemm_args(xq, xscale, xl1, wq, wscale, l2t, bias, y, M, N, K, rank, fmt)
+    dev = xq.device
+    s2 = buffer_sizes(M, max(rank2, 1), N, rank2, FMT_INT4_G64)
+    _check_buffer("inv_lambda2", inv_lambda2, 4 * N, dev)
+    _check_buffer("l1t2", l1t2, s2["l1t"], dev)
+    _check_buffer("xq2", xq2, s2["xq"], dev)
+    _check_buffer("xscale2", xscale2, s2["xscale"], dev)
+    _check_buffer("xl1_2", xl1_2, gelu_quant_xl1_bytes(M, N, rank2), dev)
     _check("w4a4_lowrank_linear_gelu_quant", lib().w4a4_lowrank_linear_gelu_quant(
         _dptr(xq), _dptr(xscale), _dptr(xl1), _dptr(wq), _dptr(wscale), _dptr(l2t), _dptr(bias), M, N, K, rank,
         _fmt(fmt), _dptr(inv_lambda2), _dptr(l1t2), rank2, _dptr(xq2), _dptr(xscale2), _dptr(xl1_2), _dptr(y),
@@ -286,7 +360,7 @@ class W4A4Linear:
         self.l2t = up(prep["l2t"], np.int16) if self.rank else None
         self.inv_lambda = up(np.asarray(inv_lambda, np.float32), np.float32)
         self.bias = None if bias_bits is None else up(np.asarray(bias_bits, np.uint16), np.int16)
-        self.device = dev
+        self.device = self.wq.device   # with its index ("cuda" -> "cuda:0")
         self._act = {}
 
     @classmethod
@@ -303,6 +377,9 @@ class W4A4Linear:
         return self._act[M]
 
     def quantize(self, x, stream=None):
+        if len(x.shape) != 2 or x.shape[1] != self.K:
+            raise ValueError(f"x has shape {tuple(x.shape)}, the layer needs [M, {self.K}]")
+        _check_matrix("x", x, 1, self.K, self.device)
         a = self.act_buffers(x.shape[0])
         quantize_act(x, self.inv_lambda, self.l1t, self.rank, self.fmt, a["xq"], a["xscale"], a["xl1"], stream)
         return a

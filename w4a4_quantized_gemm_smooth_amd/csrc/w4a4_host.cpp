@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <exception>
 #include <functional>
 #include <new>
 #include <thread>
@@ -45,21 +46,55 @@ int worker_count() {
   return int(std::max(1u, std::min(h, 16u)));
 }
 
-// Run fn(begin, end, worker) over [0, n) split into contiguous chunks, one per worker.
+// Run fn(begin, end, worker) over [0, n) split into contiguous chunks, one per worker. Exceptions
+// never escape a thread: a worker that throws records it, every thread that was started is joined
+// (also when starting a later one fails, in which case its chunk runs on the calling thread), and the
+// first recorded exception is rethrown on the calling thread, where the C ABI turns it into a status.
 void parallel_for(int n, const std::function<void(int, int, int)>& fn) {
-  int nw = std::min(worker_count(), std::max(1, n));
+  const int nw = std::min(worker_count(), std::max(1, n));
   if (nw == 1) {
     fn(0, n, 0);
     return;
   }
+  const int chunk = (n + nw - 1) / nw;
+  std::vector<std::exception_ptr> err(static_cast<size_t>(nw));
+  auto run = [&](int b, int e, int w) {
+    try {
+      fn(b, e, w);
+    } catch (...) {
+      err[w] = std::current_exception();
+    }
+  };
   std::vector<std::thread> ts;
-  int chunk = (n + nw - 1) / nw;
-  for (int w = 0; w < nw; ++w) {
-    int b = w * chunk, e = std::min(n, b + chunk);
+  ts.reserve(static_cast<size_t>(nw));
+  struct Joiner {  // joins whatever was started, on every path out of this scope
+    std::vector<std::thread>& t;
+    ~Joiner() {
+      for (auto& x : t)
+        if (x.joinable()) x.join();
+    }
+  } joiner{ts};
+  for (int w = 1; w < nw; ++w) {
+    const int b = w * chunk, e = std::min(n, b + chunk);
     if (b >= e) break;
-    ts.emplace_back(fn, b, e, w);
+    try {
+      ts.emplace_back(run, b, e, w);
+    } catch (...) {  // no thread for this chunk: run it here
+      run(b, e, w);
+    }
   }
-  for (auto& t : ts) t.join();
+  run(0, std::min(n, chunk), 0);  // the calling thread takes chunk 0
+  for (auto& x : ts) x.join();
+  for (auto& e : err)
+    if (e) std::rethrow_exception(e);
+}
+
+// true if every bf16 value of the [rows][cols] block (row stride ld) is finite
+bool all_finite_bf16(const uint16_t* a, size_t rows, size_t cols, size_t ld) {
+  for (size_t i = 0; i < rows; ++i)
+    for (size_t j = 0; j < cols; ++j)
+      if ((a[i * ld + j] & 0x7F80u) == 0x7F80u) return false;   // exponent all ones: Inf or NaN
+  return true;
 }
 
 // ------------------------------------------------------------------------------ code layouts
@@ -494,7 +529,21 @@ w4a4_status_t check_prepare_args(const uint16_t* W, int N, int K, const float* l
   if (rank > 0 && (!l1t || !l2t)) return W4A4_ERR_INVALID_ARG;
   for (int k = 0; k < K; ++k)
     if (!std::isfinite(lambda[k]) || !(lambda[k] > 0.0f)) return W4A4_ERR_INVALID_ARG;
+  if (!all_finite_bf16(W, size_t(N), size_t(K), size_t(K))) return W4A4_ERR_NUMERIC;
   return W4A4_OK;
+}
+
+// Runs a C ABI body; no C++ exception crosses the ABI: host memory exhaustion becomes
+// W4A4_ERR_HOST_MEMORY, anything else W4A4_ERR_NUMERIC.
+template <class F>
+w4a4_status_t guarded(F&& body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return W4A4_ERR_HOST_MEMORY;
+  } catch (...) {
+    return W4A4_ERR_NUMERIC;
+  }
 }
 
 }  // namespace
@@ -511,6 +560,7 @@ const char* w4a4_status_str(w4a4_status_t s) {
     case W4A4_ERR_UNSUPPORTED: return "unsupported format";
     case W4A4_ERR_NUMERIC: return "numeric error";
     case W4A4_ERR_HIP: return "HIP runtime error";
+    case W4A4_ERR_HOST_MEMORY: return "host memory allocation failed";
   }
   return "unknown status";
 }
@@ -538,22 +588,27 @@ w4a4_status_t w4a4_buffer_sizes(int M, int N, int K, int rank, int fmt, w4a4_siz
 
 w4a4_status_t w4a4_column_absmax(const uint16_t* A, int rows, int cols, int lda, float* out) {
   if (!A || !out || rows < 1 || cols < 1 || lda < cols) return W4A4_ERR_INVALID_ARG;
-  std::vector<float> acc(static_cast<size_t>(cols), 0.0f);
-  for (int i = 0; i < rows; ++i) {
-    const uint16_t* a = A + size_t(i) * lda;
-    for (int j = 0; j < cols; ++j) acc[j] = std::max(acc[j], std::fabs(bf16_to_f32(a[j])));
-  }
-  std::memcpy(out, acc.data(), sizeof(float) * size_t(cols));
-  return W4A4_OK;
+  if (!all_finite_bf16(A, size_t(rows), size_t(cols), size_t(lda))) return W4A4_ERR_NUMERIC;
+  return guarded([&] {
+    std::vector<float> acc(static_cast<size_t>(cols), 0.0f);
+    for (int i = 0; i < rows; ++i) {
+      const uint16_t* a = A + size_t(i) * lda;
+      for (int j = 0; j < cols; ++j) acc[j] = std::max(acc[j], std::fabs(bf16_to_f32(a[j])));
+    }
+    std::memcpy(out, acc.data(), sizeof(float) * size_t(cols));
+    return W4A4_OK;
+  });
 }
 
 w4a4_status_t w4a4_smooth_factors(const float* amax_x, const float* amax_w, int K, float alpha,
                                   float* lambda, float* inv_lambda) {
   if (!amax_x || !amax_w || !lambda || !inv_lambda || K < 1) return W4A4_ERR_INVALID_ARG;
   if (!(alpha > 0.0f && alpha < 1.0f)) return W4A4_ERR_INVALID_ARG;
+  return guarded([&] {
   std::vector<float> lam(static_cast<size_t>(K)), inv(static_cast<size_t>(K));
   for (int j = 0; j < K; ++j) {
     const float ax = amax_x[j], aw = amax_w[j];
+    if (!std::isfinite(ax) || !std::isfinite(aw)) return W4A4_ERR_NUMERIC;
     if (!(ax >= 0.0f) || !(aw >= 0.0f)) return W4A4_ERR_INVALID_ARG;
     float l = 1.0f;
     if (ax > 0.0f && aw > 0.0f) {
@@ -569,6 +624,7 @@ w4a4_status_t w4a4_smooth_factors(const float* amax_x, const float* amax_w, int 
   std::memcpy(lambda, lam.data(), sizeof(float) * size_t(K));
   std::memcpy(inv_lambda, inv.data(), sizeof(float) * size_t(K));
   return W4A4_OK;
+  });
 }
 
 
@@ -579,18 +635,18 @@ w4a4_status_t w4a4_prepare_weights(const uint16_t* W, int N, int K, const float*
   w4a4_status_t st = check_prepare_args(W, N, K, lambda, rank, fmt, wq, wscale, l1t, l2t);
   if (st != W4A4_OK) return st;
   if ((L1_in == nullptr) != (L2_in == nullptr)) return W4A4_ERR_INVALID_ARG;
-  try {
+  if (L1_in && rank > 0 &&
+      (!all_finite_bf16(L1_in, size_t(K), size_t(rank), size_t(rank)) ||
+       !all_finite_bf16(L2_in, size_t(rank), size_t(N), size_t(N))))
+    return W4A4_ERR_NUMERIC;
+  return guarded([&] {
     const std::vector<double> what = smoothed_weight(W, N, K, lambda);
     std::vector<uint16_t> L1, L2;
     if (!split_once(what, what.data(), N, K, rank, fmt, L1_in, L2_in, wq, wscale, L1, L2, nullptr, nullptr))
       return W4A4_ERR_NUMERIC;
     if (rank > 0) write_factors(L1, L2, N, K, rank, l1t, l2t, L1_out, L2_out);
-  } catch (const std::bad_alloc&) {
-    return W4A4_ERR_INVALID_ARG;
-  } catch (...) {
-    return W4A4_ERR_NUMERIC;
-  }
-  return W4A4_OK;
+    return W4A4_OK;
+  });
 }
 
 w4a4_status_t w4a4_prepare_weights_refined(const uint16_t* W, int N, int K, const float* lambda, int rank,
@@ -600,7 +656,7 @@ w4a4_status_t w4a4_prepare_weights_refined(const uint16_t* W, int N, int K, cons
   w4a4_status_t st = check_prepare_args(W, N, K, lambda, rank, fmt, wq, wscale, l1t, l2t);
   if (st != W4A4_OK) return st;
   if (iters < 0 || iters > 64) return W4A4_ERR_INVALID_ARG;
-  try {
+  return guarded([&] {
     const int np = rows_pad_of(N), G = K / W4A4_GROUP;
     const bool mx = fmt == W4A4_FMT_MXFP4_B32, w8 = fmt == W4A4_FMT_W8A8;
     const size_t q_bytes = w8 ? size_t(np) * K : size_t(np) * K / 2;
@@ -627,23 +683,22 @@ w4a4_status_t w4a4_prepare_weights_refined(const uint16_t* W, int N, int K, cons
       for (size_t i = 0; i < target.size(); ++i) target[i] = what[i] - deq[i];
     }
     if (best_iter) *best_iter = best_it;
-  } catch (const std::bad_alloc&) {
-    return W4A4_ERR_INVALID_ARG;
-  } catch (...) {
-    return W4A4_ERR_NUMERIC;
-  }
-  return W4A4_OK;
+    return W4A4_OK;
+  });
 }
 
 w4a4_status_t w4a4_append_lowrank(const uint16_t* l1t, const uint16_t* l2t, int K, int N, int rank,
                                   const uint16_t* A, const uint16_t* B, int ra,
                                   uint16_t* l1t_out, uint16_t* l2t_out) {
-  if (!A || !B || !l1t_out || !l2t_out || ra < 1) return W4A4_ERR_INVALID_ARG;
+  if (!A || !B || !l1t_out || !l2t_out || ra < 1 || rank < 0 || ra > W4A4_MAX_RANK) return W4A4_ERR_INVALID_ARG;
   if (rank > 0 && (!l1t || !l2t)) return W4A4_ERR_INVALID_ARG;
   const int r2 = rank + ra;
   w4a4_status_t st = check_shape(1, N, K, r2, W4A4_FMT_INT4_G64);
   if (st != W4A4_OK) return st;
+  if (!all_finite_bf16(A, size_t(K), size_t(ra), size_t(ra)) || !all_finite_bf16(B, size_t(ra), size_t(N), size_t(N)))
+    return W4A4_ERR_NUMERIC;
   const int np = rows_pad_of(N), rp = rank_pad_of(rank), rp2 = rank_pad_of(r2);
+  return guarded([&] {
   std::vector<uint16_t> o1(size_t(rp2) * K, 0), o2(size_t(np) * rp2, 0);
   for (int i = 0; i < rank; ++i) std::memcpy(&o1[size_t(i) * K], &l1t[size_t(i) * K], size_t(K) * 2);
   for (int i = 0; i < ra; ++i)
@@ -655,6 +710,7 @@ w4a4_status_t w4a4_append_lowrank(const uint16_t* l1t, const uint16_t* l2t, int 
   std::memcpy(l1t_out, o1.data(), o1.size() * 2);
   std::memcpy(l2t_out, o2.data(), o2.size() * 2);
   return W4A4_OK;
+  });
 }
 
 w4a4_status_t w4a4_codes_to_canonical(const uint8_t* q, int rows, int K, int fmt, uint8_t* out) {

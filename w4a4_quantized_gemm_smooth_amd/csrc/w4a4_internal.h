@@ -2,6 +2,7 @@
 // libw4a4. Not part of the public ABI.
 #pragma once
 
+#include <climits>
 #include <cstddef>
 #include <cstdint>
 
@@ -21,6 +22,8 @@ inline bool fmt_known(int fmt) {
 inline w4a4_status_t check_shape(int M, int N, int K, int rank, int fmt) {
   if (!fmt_known(fmt)) return W4A4_ERR_UNSUPPORTED;
   if (M < 1 || N < 1 || K < W4A4_GROUP || K % W4A4_GROUP != 0) return W4A4_ERR_INVALID_ARG;
+  // rows are padded to a multiple of W4A4_ROW_ALIGN in int arithmetic: keep that from overflowing
+  if (M > INT_MAX - W4A4_ROW_ALIGN || N > INT_MAX - W4A4_ROW_ALIGN) return W4A4_ERR_INVALID_ARG;
   if (rank < 0 || rank > W4A4_MAX_RANK || rank > N || rank > K) return W4A4_ERR_INVALID_ARG;
   // W8A8: the int32 dot product of 127-bounded codes must not overflow, and the one-byte codes
   // (rows_pad * K bytes per operand) must stay below 2^31 bytes
