@@ -51,6 +51,7 @@ extern "C" {
 #define W4A4_RANK_ALIGN 16   /* rank is zero-padded to a multiple of this (r_pad) */
 #define W4A4_MAX_RANK 128    /* largest supported rank (after any LoRA merge) */
 #define W4A4_W8A8_MAX_K 131072 /* W8A8: 127 * 127 * K stays below 2^31 (exact int32 sums) */
+#define W4A4_NOALLOC_SCRATCH_BYTES (32u << 20) /* fixed per-GPU scratch of the no-allocation call */
 
 typedef enum {
   W4A4_OK = 0,
@@ -58,7 +59,8 @@ typedef enum {
   W4A4_ERR_UNSUPPORTED = 2,  /* unknown format */
   W4A4_ERR_NUMERIC = 3,      /* non-finite input, non-normal smoothing factor, SVD failure */
   W4A4_ERR_HIP = 4,          /* a HIP launch or runtime call failed */
-  W4A4_ERR_HOST_MEMORY = 5   /* a host-side allocation failed */
+  W4A4_ERR_HOST_MEMORY = 5,  /* a host-side allocation failed */
+  W4A4_ERR_TOO_LARGE = 6     /* the problem needs more than the no-allocation call's fixed scratch */
 } w4a4_status_t;
 
 typedef enum {
@@ -267,6 +269,29 @@ w4a4_status_t w4a4_lowrank_linear_gelu_quant(const uint8_t* xq, const void* xsca
 
 /* Bytes of the xl1_2 buffer of w4a4_lowrank_linear_gelu_quant (0 when rank2 < 1 or M, N < 1). */
 size_t w4a4_gelu_quant_xl1_bytes(int M, int N, int rank2);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): w4a4_lowrank_linear_gelu_quant without any
+ * caller-provided scratch. Same arguments and results, except that t2 is only fc2's t
+ * ([m_pad][rank2_pad] fp32, m_pad * rank2_pad * 4 bytes) and the per-256-column-tile partial t2
+ * planes go to a fixed device array owned by the library: W4A4_NOALLOC_SCRATCH_BYTES on every GPU
+ * the library runs on, from the loading of its code on that GPU until the process ends. The call
+ * allocates nothing (no hipMalloc, no allocating library routine); its first call on a GPU looks
+ * up that GPU's copy of the array (hipGetSymbolAddress) with the GPU current.
+ * Limit: ceil(N / 256) * m_pad * rank2_pad * 4 bytes must not exceed W4A4_NOALLOC_SCRATCH_BYTES
+ * (e.g. M = 4608, N = 12288, rank2 = 32: 28.3 MB), else W4A4_ERR_TOO_LARGE before anything is
+ * launched. Every call writes all the planes it reads, so nothing needs clearing between calls;
+ * but all calls on one GPU share that GPU's array, so calls that overlap in time on one GPU (other
+ * streams, other threads) race, and the caller must serialize them. W4A4_ERR_HIP if the array's
+ * address cannot be looked up or a launch fails.
+ */
+w4a4_status_t w4a4_lowrank_linear_gelu_quant_noalloc(const uint8_t* xq, const void* xscale, const float* xl1,
+                                                     const uint8_t* wq, const void* wscale, const uint16_t* l2t,
+                                                     const uint16_t* bias, int M, int N, int K, int rank, int fmt,
+                                                     const float* inv_lambda2, const uint16_t* l1t2, int rank2,
+                                                     uint8_t* xq2, void* xscale2, float* t2, uint16_t* Y, int ldy,
+                                                     w4a4_stream_t stream);
 
 #ifdef __cplusplus
 }

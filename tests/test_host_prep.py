@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "w4a4.h")
 
 def test_library_exports_every_declared_symbol():
     decl = set(re.findall(r"\b(w4a4_[a-z0-9_]+)\s*\(", open(HEADER).read()))
-    assert len(decl) == 15, sorted(decl)
+    assert len(decl) == 16, sorted(decl)
     L = w4.lib()
     missing = [n for n in decl if not hasattr(L, n)]
     assert not missing, missing
@@ -446,3 +446,21 @@ def test_host_half_under_address_and_undefined_behaviour_sanitizers(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=600)
     assert run.returncode == 0, (run.stdout[-2000:], run.stderr[-4000:])
     assert "host half OK" in run.stdout
+
+
+def test_noalloc_entry_point_rejects_before_touching_the_gpu():
+    """The no-allocation MLP call checks its arguments, and that the partial planes fit its fixed
+    scratch, before anything else (no GPU is present here)."""
+    L = w4.lib()
+    al = np.zeros(1 << 12, np.uint8)
+    base = al.ctypes.data + (-al.ctypes.data) % 256
+    P = lambda off=0: ctypes.c_void_p(base + off)
+    f = L.w4a4_lowrank_linear_gelu_quant_noalloc
+    # planes: ceil(N / 256) * m_pad * rank2_pad * 4 bytes > 32 MiB -> W4A4_ERR_TOO_LARGE (6)
+    M, N = 16384, 4096                      # 16 tiles * 16384 * 32 * 4 = 32 MiB + ... > limit at rank2 32
+    assert 16 * 16384 * 32 * 4 >= w4.NOALLOC_SCRATCH_BYTES
+    assert f(P(), P(), None, P(), P(), None, None, M + 256, N, 64, 0, 0, P(), P(), 32, P(), P(), P(), None, 0, None) == 6
+    assert f(P(), P(), None, P(), P(), None, None, 4, 128, 64, 0, 1, P(), None, 0, P(), P(), None, None, 0, None) == 2
+    assert f(P(), P(), None, P(), P(), None, None, 4, 96, 64, 0, 0, P(), None, 0, P(), P(), None, None, 0, None) == 1
+    assert f(P(), P(), None, P(), P(), None, None, 4, 128, 64, 0, 0, P(), None, 8, P(), P(), None, None, 0, None) == 1
+    assert L.w4a4_status_str(6) == b"problem exceeds the no-allocation call's fixed scratch"

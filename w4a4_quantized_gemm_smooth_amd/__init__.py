@@ -23,6 +23,7 @@ __all__ = [
     "buffer_sizes", "column_absmax", "smooth_factors", "prepare_weights", "append_lowrank",
     "codes_to_canonical", "scales_to_canonical", "quantize_act", "lowrank_linear", "W4A4Linear",
     "FMT_W8A8", "gelu_quantize_act", "lowrank_linear_gelu_quant", "gelu_quant_xl1_bytes", "MLPPair",
+    "lowrank_linear_gelu_quant_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 FMT_INT4_G64 = 0
@@ -34,6 +35,7 @@ ROW_ALIGN = 256
 RANK_ALIGN = 16
 MAX_RANK = 128
 W8A8_MAX_K = 131072
+NOALLOC_SCRATCH_BYTES = 32 << 20
 _FMT_NAMES = {"int4_g64": FMT_INT4_G64, "mxfp4_b32": FMT_MXFP4_B32, "w8a8": FMT_W8A8}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "w4a4_lowrank_linear": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P],
             "w4a4_gelu_quantize_act": [P, I, I, I, P, P, I, I, P, P, P, P],
             "w4a4_lowrank_linear_gelu_quant": [P, P, P, P, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, I, P],
+            "w4a4_lowrank_linear_gelu_quant_noalloc": [P, P, P, P, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, I, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -336,6 +339,25 @@ def lowrank_linear_gelu_quant(xq, xscale, xl1, wq, wscale, l2t, bias, M, N, K, r
     _check("w4a4_lowrank_linear_gelu_quant", lib().w4a4_lowrank_linear_gelu_quant(
         _dptr(xq), _dptr(xscale), _dptr(xl1), _dptr(wq), _dptr(wscale), _dptr(l2t), _dptr(bias), M, N, K, rank,
         _fmt(fmt), _dptr(inv_lambda2), _dptr(l1t2), rank2, _dptr(xq2), _dptr(xscale2), _dptr(xl1_2), _dptr(y),
+        0 if y is None else y.stride(0), _stream(stream)))
+
+
+def lowrank_linear_gelu_quant_noalloc(xq, xscale, xl1, wq, wscale, l2t, bias, M, N, K, rank, fmt, inv_lambda2, l1t2,
+                                      rank2, xq2, xscale2, t2, y=None, stream=None):
+    """As ``lowrank_linear_gelu_quant``, but t2 holds only fc2's t ([m_pad, rank2_pad] fp32) and the
+    library keeps the partial planes in its fixed per-GPU scratch (no allocation anywhere; calls that
+    overlap on one GPU race)."""
+    _check_gemm_args(xq, xscale, xl1, wq, wscale, l2t, bias, y, M, N, K, rank, fmt)
+    dev = xq.device
+    s2 = buffer_sizes(M, max(rank2, 1), N, rank2, FMT_INT4_G64)
+    _check_buffer("inv_lambda2", inv_lambda2, 4 * N, dev)
+    _check_buffer("l1t2", l1t2, s2["l1t"], dev)
+    _check_buffer("xq2", xq2, s2["xq"], dev)
+    _check_buffer("xscale2", xscale2, s2["xscale"], dev)
+    _check_buffer("t2", t2, s2["m_pad"] * s2["rank_pad"] * 4, dev)
+    _check("w4a4_lowrank_linear_gelu_quant_noalloc", lib().w4a4_lowrank_linear_gelu_quant_noalloc(
+        _dptr(xq), _dptr(xscale), _dptr(xl1), _dptr(wq), _dptr(wscale), _dptr(l2t), _dptr(bias), M, N, K, rank,
+        _fmt(fmt), _dptr(inv_lambda2), _dptr(l1t2), rank2, _dptr(xq2), _dptr(xscale2), _dptr(t2), _dptr(y),
         0 if y is None else y.stride(0), _stream(stream)))
 
 

@@ -27,6 +27,8 @@
 //  * The low-rank branch uses the bf16 MFMAs (16x16x32 for the down projection, 32x32x16 for the
 //    up projection, accumulating straight into the GEMM accumulators).
 
+#include <mutex>
+
 #include "w4a4_device_common.h"
 
 using namespace w4a4;
@@ -1164,12 +1166,15 @@ w4a4_status_t w4a4_gelu_quantize_act(const uint16_t* Y, int M, int K, int ldy, c
   return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP;
 }
 
-w4a4_status_t w4a4_lowrank_linear_gelu_quant(const uint8_t* xq, const void* xscale, const float* xl1,
-                                             const uint8_t* wq, const void* wscale, const uint16_t* l2t,
-                                             const uint16_t* bias, int M, int N, int K, int rank, int fmt,
-                                             const float* inv_lambda2, const uint16_t* l1t2, int rank2,
-                                             uint8_t* xq2, void* xscale2, float* xl1_2, uint16_t* Y, int ldy,
-                                             w4a4_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the two entry points of the producer-side MLP GEMM.
+w4a4_status_t check_gelu_quant_args(const uint8_t* xq, const void* xscale, const float* xl1, const uint8_t* wq,
+                                    const void* wscale, const uint16_t* l2t, const uint16_t* bias, int M, int N,
+                                    int K, int rank, int fmt, const float* inv_lambda2, const uint16_t* l1t2,
+                                    int rank2, uint8_t* xq2, void* xscale2, float* xl1_2, uint16_t* Y, int ldy) {
   w4a4_status_t st = check_shape(M, N, K, rank, fmt);
   if (st != W4A4_OK) return st;
   if (fmt != W4A4_FMT_INT4_G64 || rank > 32 || rank2 > 32) return W4A4_ERR_UNSUPPORTED;
@@ -1183,12 +1188,84 @@ w4a4_status_t w4a4_lowrank_linear_gelu_quant(const uint8_t* xq, const void* xsca
   if (rank2 > 0 && (!l1t2 || !xl1_2 || !aligned16(l1t2) || !aligned16(xl1_2))) return W4A4_ERR_INVALID_ARG;
   if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return W4A4_ERR_INVALID_ARG;
   if (Y && ((reinterpret_cast<uintptr_t>(Y) & 1u) || ldy < N)) return W4A4_ERR_INVALID_ARG;
+  return W4A4_OK;
+}
+
+// The no-allocation entry point's scratch: fc2's per-256-column-tile partial t planes live in this
+// fixed array (one copy per GPU, from the loading of this code object until the process ends).
+// In host code `scratch` names a host-side stand-in, not device memory: kernels and copies use the
+// per-device address taken with hipGetSymbolAddress below, never the name.
+constexpr size_t NOALLOC_SCRATCH_FLOATS = size_t(W4A4_NOALLOC_SCRATCH_BYTES) / sizeof(float);
+static __device__ __attribute__((aligned(256))) float scratch[NOALLOC_SCRATCH_FLOATS];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::once_flag scratch_once[SCRATCH_MAX_DEVICES];
+float* scratch_addr[SCRATCH_MAX_DEVICES];
+hipError_t scratch_status[SCRATCH_MAX_DEVICES];
+
+// The current device's address of `scratch`, looked up once per device with that device current.
+hipError_t scratch_of_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+  try {
+    std::call_once(scratch_once[dev], [dev] {
+      void* p = nullptr;
+      scratch_status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      scratch_addr[dev] = static_cast<float*>(p);
+    });
+  } catch (...) {  // std::call_once reports a failed synchronization by throwing
+    return hipErrorUnknown;
+  }
+  if (scratch_status[dev] != hipSuccess) return scratch_status[dev];
+  if (!scratch_addr[dev]) return hipErrorInvalidSymbol;
+  *out = scratch_addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a4_status_t w4a4_lowrank_linear_gelu_quant(const uint8_t* xq, const void* xscale, const float* xl1,
+                                             const uint8_t* wq, const void* wscale, const uint16_t* l2t,
+                                             const uint16_t* bias, int M, int N, int K, int rank, int fmt,
+                                             const float* inv_lambda2, const uint16_t* l1t2, int rank2,
+                                             uint8_t* xq2, void* xscale2, float* xl1_2, uint16_t* Y, int ldy,
+                                             w4a4_stream_t stream) {
+  const w4a4_status_t st = check_gelu_quant_args(xq, xscale, xl1, wq, wscale, l2t, bias, M, N, K, rank, fmt,
+                                                 inv_lambda2, l1t2, rank2, xq2, xscale2, xl1_2, Y, ldy);
+  if (st != W4A4_OK) return st;
   const int m_pad = rows_pad_of(M), n_pad = rows_pad_of(N), rp2 = rank_pad_of(rank2);
   const int tiles_n = n_pad / 256;
   GeluQuantArgs fa{inv_lambda2, l1t2, xq2, static_cast<uint16_t*>(xscale2),
                    rank2 > 0 ? (tiles_n > 1 ? xl1_2 + (size_t)m_pad * rp2 : xl1_2) : nullptr};
   const hipError_t e = dispatch_gemm_gelu_quant(rank_pad_of(rank) / 16, rp2 / 16, xq, xscale, xl1, wq, wscale, l2t,
                                                 bias, Y, ldy, M, N, K, m_pad, n_pad, fa, xl1_2,
+                                                reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP;
+}
+
+w4a4_status_t w4a4_lowrank_linear_gelu_quant_noalloc(const uint8_t* xq, const void* xscale, const float* xl1,
+                                                     const uint8_t* wq, const void* wscale, const uint16_t* l2t,
+                                                     const uint16_t* bias, int M, int N, int K, int rank, int fmt,
+                                                     const float* inv_lambda2, const uint16_t* l1t2, int rank2,
+                                                     uint8_t* xq2, void* xscale2, float* t2, uint16_t* Y, int ldy,
+                                                     w4a4_stream_t stream) {
+  const w4a4_status_t st = check_gelu_quant_args(xq, xscale, xl1, wq, wscale, l2t, bias, M, N, K, rank, fmt,
+                                                 inv_lambda2, l1t2, rank2, xq2, xscale2, t2, Y, ldy);
+  if (st != W4A4_OK) return st;
+  const int m_pad = rows_pad_of(M), n_pad = rows_pad_of(N), rp2 = rank_pad_of(rank2);
+  const int tiles_n = n_pad / 256;
+  const bool planes = rank2 > 0 && tiles_n > 1;  // one tile writes t2 itself, no plane needed
+  if (planes && size_t(tiles_n) * size_t(m_pad) * size_t(rp2) > NOALLOC_SCRATCH_FLOATS) return W4A4_ERR_TOO_LARGE;
+  float* part = nullptr;
+  if (planes && scratch_of_current_device(&part) != hipSuccess) return W4A4_ERR_HIP;
+  GeluQuantArgs fa{inv_lambda2, l1t2, xq2, static_cast<uint16_t*>(xscale2),
+                   rank2 > 0 ? (planes ? part : t2) : nullptr};
+  const hipError_t e = dispatch_gemm_gelu_quant(rank_pad_of(rank) / 16, rp2 / 16, xq, xscale, xl1, wq, wscale, l2t,
+                                                bias, Y, ldy, M, N, K, m_pad, n_pad, fa, t2,
                                                 reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP;
 }

@@ -561,6 +561,7 @@ const char* w4a4_status_str(w4a4_status_t s) {
     case W4A4_ERR_NUMERIC: return "numeric error";
     case W4A4_ERR_HIP: return "HIP runtime error";
     case W4A4_ERR_HOST_MEMORY: return "host memory allocation failed";
+    case W4A4_ERR_TOO_LARGE: return "problem exceeds the no-allocation call's fixed scratch";
   }
   return "unknown status";
 }
