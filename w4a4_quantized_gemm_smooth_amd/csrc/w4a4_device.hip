@@ -108,42 +108,112 @@ __device__ __forceinline__ uint2 quant_int4_lane(const float (&xh)[2][8], uint32
 }
 
 // ===================================================================================
-// Kernel 1: activation side. Per row and group: X̂ = fp32(x * inv_lambda); codes + scales (W8A8:
-// the row's running max|X̂| instead, written per slice for the second W8A8 pass);
-// t += bf16(X̂) · L1 (MFMA). One block = 128 rows (8 waves of 16) x one slice of at most
-// QA_MAX_GS groups: every wave issues the X loads of all its groups at once, and the slice's
-// 1/λ and L1 rows are copied into LDS by the LDS DMA path, shared by the 8 row tiles. With
-// several slices the partial t of a slice goes to its own scratch plane; t_reduce_kernel sums
-// the planes in slice order.
+// Kernel 1: activation side. Per row and group: X̂ = fp32(x · (1/λ)); codes + scales (W8A8: the
+// row's running max|X̂| instead, written per slice for the second W8A8 pass); t += bf16(X̂)·L1
+// (MFMA). One block = 64 rows (4 waves of 16) x one slice of at most QA_MAX_GS groups, so the
+// slice's L1 rows are fetched once per 64 rows: they and the slice's 1/λ are copied into LDS by the
+// LDS DMA path, and every wave issues the X loads of all its groups at once (buffer loads over the
+// wave's rows: rows past M and groups past the slice read as zeros, so padding rows come out as zero
+// codes, scales and t without any per-row select). With several slices the partial t of a slice
+// goes to its own plane and t_reduce_kernel sums the planes in slice order (deterministic; a
+// reduction inside one kernel would need device-scope release fences, which write back the per-XCD
+// L2s). Lane (r, kc) = (lane & 15, lane >> 4) owns row r of its wave's rows and the values
+// 16 kc .. 16 kc + 15 of each group; each lane reads one 1/λ value per group and the DPP row
+// broadcast hands value e of its 16-lane row straight to the multiply of element e. INT4: the
+// row's group maximum over its four lanes by two lane swaps, s = bf16(max/7), y = fp32(X̂ · (1/s)),
+// and one FP6 conversion emits the codes of two groups (32 values) at once; MXFP4: E8M0 exponent
+// and E2M1 codes. The down projection runs on 16x16x32 bf16 MFMAs with L1 from LDS.
 // ===================================================================================
 constexpr int QA_WAVES = QA_BLOCK_ROWS / 16;
 
+// Exact shortcuts for the two divisions of the INT4 group quantizer. Both were checked
+// exhaustively on the host against IEEE division (this file is built with fp32 denormals preserved,
+// which the first one needs for tiny maxima):
+//  * s = bf16(amax / 7), flushed to 0 below 2^-126: the product amax · fp32(1/7) corrected once by
+//    its exact fma residual rounds to the same s as the IEEE quotient, for every finite amax >= 0;
+//  * 1/s for a bf16 scale s >= 2^-126: one Newton step y0 + y0 · fma(−s, y0, 1) from any y0 within
+//    one ulp of 1/s (v_rcp_f32 is) is the correctly rounded reciprocal.
+__device__ __forceinline__ float int4_scale(float amax) {
+  constexpr float c = 1.0f / 7.0f;
+  const float q0 = amax * c;
+  const float q = __builtin_fmaf(__builtin_fmaf(-7.0f, q0, amax), c, q0);
+  const float s = bf16f(bf16_rne(q));
+  return s >= 0x1p-126f ? s : 0.f;
+}
+__device__ __forceinline__ float int4_recip(float s) {  // 0 for s == 0
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  const float y = __builtin_fmaf(__builtin_fmaf(-s, y0, 1.0f), y0, y0);
+  return s != 0.f ? y : 0.f;
+}
+
+// max over the four lanes r, r+16, r+32, r+48 (one group row): two gfx950 lane swaps
+__device__ __forceinline__ float max_over_kc(float m) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// max over lanes r + 16 kc and r + 16 (kc ^ 1) (the two lanes of one MX 32-block)
+__device__ __forceinline__ float max_over_kc_pair(float m) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// X̂ of two groups for this lane: 2 x 16 bf16 values (two 16-byte loads each) times 1/λ, value e's
+// factor taken from lane e of the lane's 16-lane row by a DPP row broadcast folded into the
+// multiply. Every value is unpacked before the first multiply: a DPP instruction may not read a
+// register that the previous two VALU instructions wrote.
+template <int E = 0>
+__device__ __forceinline__ void scale_pair(const float (&ua)[16], const float (&ub)[16], uint32_t ila, uint32_t ilb,
+                                           float (&xa)[16], float (&xb)[16]) {
+  if constexpr (E < 16) {
+    xa[E] = ua[E] * __int_as_float(__builtin_amdgcn_mov_dpp((int)ila, 0x150 + E, 0xF, 0xF, true));
+    xb[E] = ub[E] * __int_as_float(__builtin_amdgcn_mov_dpp((int)ilb, 0x150 + E, 0xF, 0xF, true));
+    scale_pair<E + 1>(ua, ub, ila, ilb, xa, xb);
+  }
+}
+
+template <bool GELU_IN>
+__device__ __forceinline__ void unpack16(const v4i (&xv)[2], float (&u)[16]) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t w = (uint32_t)xv[e >> 3][(e >> 1) & 3];
+    uint32_t bits = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+    if (GELU_IN) bits = bf16_rne(gelu32(bf16f(bits)));
+    u[e] = bf16f(bits);
+  }
+}
+
+// X̂ = fp32(x · (1/λ)), one fp32 multiply per value (no contraction: nothing to fuse)
+template <bool GELU_IN>
+__device__ __forceinline__ void smooth_pair(const v4i (&xva)[2], const v4i (&xvb)[2], uint32_t ila, uint32_t ilb,
+                                            float (&xa)[16], float (&xb)[16]) {
+  float ua[16], ub[16];
+  unpack16<GELU_IN>(xva, ua);
+  unpack16<GELU_IN>(xvb, ub);
+  scale_pair(ua, ub, ila, ilb, xa, xb);
+}
 
 // LDS bytes of one block: 1/λ (16 B slots), L1 rows of RP rank columns padded by one slot, in
 // whole 64-slot DMA instructions
 constexpr int qa_lds_slots(int rp, int gs) { return (gs * 16 + rp * (gs * 8 + 1) + 63) / 64 * 64; }
 
-// GELU_IN: the input is a producer's bf16 output Y and the layer's activations are
-// X = bf16(GELU(Y)) (the MLP's fc2; INT4 only)
 template <int FMT, int NT, bool GELU_IN = false>  // NT = rank_pad / 16 (0 when there is no low-rank branch)
-__global__ __launch_bounds__(QA_WAVES * 64, NT <= 2 ? 4 : 2) void quantize_act_kernel(
-    // X is not restrict: its loads must stay ahead of the counted wait below
+__global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
     const uint16_t* X, int M, int K, int ldx, const float* __restrict__ inv_lambda,
     const uint16_t* __restrict__ l1t, int m_pad, int gs, uint8_t* __restrict__ xq, void* __restrict__ xscale,
     float* __restrict__ xl1) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int RP = NT * 16;
+  constexpr int RP = NT * 16, NTA = NT > 0 ? NT : 1;
   const int G = K / W4A4_GROUP;
   const int nsl = (G + gs - 1) / gs;
   const int rb = blockIdx.x / nsl, sl = blockIdx.x % nsl;
   const int g0 = sl * gs, ng = min(gs, G - g0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // lane (r, kc) owns row r of the wave's tile and the 16 consecutive values 16 kc .. 16 kc + 15
-  // of each group
   const int r = lane & 15, kc = lane >> 4;
-  const int row = rb * QA_BLOCK_ROWS + wave * 16 + r;
-  const bool valid = row < M;
+  const int row0 = rb * QA_BLOCK_ROWS + wave * 16, row = row0 + r;
 
   // ---- 1. 1/λ and L1 rows of the slice -> LDS. Slot s (16 B) of the block's LDS: s < 16 ng are
   // 1/λ; then rank row c uses slots [16 ng + c (8 ng + 1), +8 ng + 1) for k = 64 g0 .. 64 (g0 + ng),
@@ -159,99 +229,51 @@ __global__ __launch_bounds__(QA_WAVES * 64, NT <= 2 ? 4 : 2) void quantize_act_k
     __builtin_amdgcn_global_load_lds(src, smem + 16 * s0, 16, 0, 0);
   }
 
-  // ---- 2. X of every group of the slice, straight into registers: exactly 2 * QA_MAX_GS loads
-  // per wave after the DMA, unconditional (rows past M read row M-1 and are zeroed at use, groups
-  // past the slice reload its last group), so vmcnt(2 QA_MAX_GS) means the DMA has landed while
-  // the X loads may still be in flight
-  const uint16_t* xrow = X + (size_t)min(row, M - 1) * ldx + (size_t)g0 * W4A4_GROUP + kc * 16;
-  uint4 xv[QA_MAX_GS][2];
+  // ---- 2. X of every group of the slice, straight into registers: exactly 2 * QA_MAX_GS buffer
+  // loads per wave after the DMA (rows past M and groups past the slice read as zeros), so
+  // vmcnt(2 QA_MAX_GS) means the DMA has landed while the X loads may still be in flight. Every part
+  // of the resource is wave-uniform; readfirstlane keeps it in scalar registers.
+  const int valid = __builtin_amdgcn_readfirstlane(max(0, min(16, M - row0)));
+  const uint64_t xbase = reinterpret_cast<uint64_t>(valid > 0 ? X + (size_t)row0 * ldx : X);
+  const uint64_t xb_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)xbase);
+  const uint64_t xb_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(xbase >> 32));
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(xb_lo | (xb_hi << 32)), 0, __builtin_amdgcn_readfirstlane(valid * ldx * 2), 0x00020000);
+  constexpr int OOB = 0x7FFFFF00;  // an offset past every buffer: loads read zeros, stores are dropped
+  v4i xv[QA_MAX_GS][2];
 #pragma unroll
-  for (int i = 0; i < QA_MAX_GS; ++i)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) xv[i][h] = *reinterpret_cast<const uint4*>(xrow + min(i, ng - 1) * W4A4_GROUP + 8 * h);
+  for (int i = 0; i < QA_MAX_GS; ++i) {
+    const int off = i < ng ? (r * ldx + (g0 + i) * W4A4_GROUP + kc * 16) * 2 : OOB;
+    xv[i][0] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+    xv[i][1] = __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16, 0, 0);
+  }
   asm volatile("" ::: "memory");  // the loads stay ahead of the wait that counts them
   wait_vmcnt<2 * QA_MAX_GS>();
   __builtin_amdgcn_s_barrier();
-  const float* s_il = reinterpret_cast<const float*>(smem);
+  const uint32_t* s_il = reinterpret_cast<const uint32_t*>(smem);
   const uint8_t* s_l1 = smem + 16 * n_il;
   const int l1_stride = 16 * l1_row;
 
-  constexpr int NTA = NT > 0 ? NT : 1;
-  float row_amax = 0.f;  // W8A8: running max|X̂| of the lane's values
+  // the outputs as buffers: a store whose offset lies past the buffer is dropped, so a pair without
+  // its second group needs no branch
+  const int G2 = FMT == W4A4_FMT_MXFP4_B32 ? 2 * G : G;  // scale planes
+  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(xq, 0, G * m_pad * 32, 0x00020000);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      xscale, 0, FMT == W4A4_FMT_W8A8 ? 0 : G2 * m_pad * (FMT == W4A4_FMT_INT4_G64 ? 2 : 1), 0x00020000);
+
   v4f acc[NTA];
 #pragma unroll
   for (int c = 0; c < NTA; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int i = 0; i < QA_MAX_GS; ++i) {
-    if (i >= ng) break;  // block-uniform
-    const int g = g0 + i;
-    const float* il = s_il + i * W4A4_GROUP + kc * 16;
-    float xh[2][8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float4 i0 = *reinterpret_cast<const float4*>(il + 8 * h);
-      const float4 i1 = *reinterpret_cast<const float4*>(il + 8 * h + 4);
-      const uint32_t xw[4] = {valid ? xv[i][h].x : 0u, valid ? xv[i][h].y : 0u, valid ? xv[i][h].z : 0u,
-                              valid ? xv[i][h].w : 0u};
-      const float ilv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t bits = (e & 1) ? (xw[e >> 1] >> 16) : (xw[e >> 1] & 0xFFFFu);
-        if (GELU_IN) bits = bf16_rne(gelu32(bf16f(bits)));
-        xh[h][e] = bf16f(bits) * ilv[e];  // one fp32 multiply (no contraction: nothing to fuse)
-      }
-    }
-    uint2* qdst = reinterpret_cast<uint2*>(xq + ((size_t)g * m_pad + row) * 32 + kc * 8);
-    if constexpr (FMT == W4A4_FMT_W8A8) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) row_amax = fmaxf(row_amax, fabsf(xh[h][e]));
-    } else if constexpr (FMT == W4A4_FMT_INT4_G64) {
-      uint32_t sb;
-      *qdst = quant_int4_lane(xh, sb);
-      if (kc == 0) static_cast<uint16_t*>(xscale)[(size_t)g * m_pad + row] = (uint16_t)sb;
-    } else {
-      // the lane's 16 values lie in 32-block kc / 2, shared with lane kc ^ 1
-      float amax = 0.f;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xh[h][e]));
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      int e8;
-      if (amax == 0.f) {
-        e8 = -127;
-      } else {
-        int ex;
-        const float mant = frexpf(amax, &ex);  // amax = mant * 2^ex, mant in [0.5, 1)
-        e8 = mant <= 0.75f ? ex - 3 : ex - 2;
-        e8 = max(-127, min(127, e8));
-      }
-      // E2M1 nearest-even of X̂ * 2^-e (exact scaling), sign kept for values that round to
-      // zero: v_cvt_scalef32_pk_fp4_f32 with scale 1 puts codes k, k+1 into byte k/2
-      uint32_t word[2] = {0u, 0u};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float z[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = ldexpf(xh[h][e], -e8);
-        word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[0], z[1], 1.0f, 0);
-        word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[2], z[3], 1.0f, 1);
-        word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[4], z[5], 1.0f, 2);
-        word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[6], z[7], 1.0f, 3);
-      }
-      *qdst = make_uint2(word[0], word[1]);
-      if ((kc & 1) == 0)
-        static_cast<uint8_t*>(xscale)[(size_t)(2 * g + (kc >> 1)) * m_pad + row] = (uint8_t)(e8 + 127);
-    }
-    if (NT > 0) {
+  float row_amax = 0.f;  // W8A8: running max|X̂| of the lane's values
+  // t += bf16(X̂)·L1 for group i of the slice: the lane's 8 values of half h are the A operand's k
+  // slots 8 (lane / 16) .., paired with the same k of L1 (from LDS) in the B operand
+  auto down = [&](const float (&xh)[16], int i) {
+    if constexpr (NT > 0) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         v4i a;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) a[d] = (int)pack_bf16x2(xh[h][2 * d], xh[h][2 * d + 1]);
+        for (int d = 0; d < 4; ++d) a[d] = (int)pack_bf16x2(xh[8 * h + 2 * d], xh[8 * h + 2 * d + 1]);
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
           const v4i b = *reinterpret_cast<const v4i*>(s_l1 + (c * 16 + r) * l1_stride + i * 128 + kc * 32 + 16 * h);
@@ -259,17 +281,103 @@ __global__ __launch_bounds__(QA_WAVES * 64, NT <= 2 ? 4 : 2) void quantize_act_k
         }
       }
     }
+  };
+
+#pragma unroll
+  for (int i = 0; i < QA_MAX_GS; i += 2) {
+    if (i >= ng) break;  // block-uniform
+    const bool two = i + 1 < ng;
+    const int ga = g0 + i, gb = ga + 1;
+    // this lane's 1/λ of both groups (a missing second group reads the first's: its X is zero)
+    const uint32_t ila = s_il[i * W4A4_GROUP + kc * 16 + r];
+    const uint32_t ilb = s_il[min(i + 1, ng - 1) * W4A4_GROUP + kc * 16 + r];
+    float xa[16], xb[16];  // group gb is all zeros when the slice has no such group
+    smooth_pair<GELU_IN>(xv[i], xv[i + 1], ila, ilb, xa, xb);
+    if constexpr (FMT == W4A4_FMT_INT4_G64) {
+      float ma = 0.f, mb = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        ma = fmaxf(ma, fabsf(xa[e]));
+        mb = fmaxf(mb, fabsf(xb[e]));
+      }
+      const float sa = int4_scale(max_over_kc(ma)), sb = int4_scale(max_over_kc(mb));
+      const float ia = int4_recip(sa), ib = int4_recip(sb);
+      // y = X̂ · (1/s); v_cvt_scalef32_2xpk16_fp6_f32 rounds y / 8 to nearest-even on the E2M3
+      // subnormal grid (step 1/8), i.e. emits the carrier field sign|00|rint(y) (|y| < 7.5 by the
+      // symmetric scale). Sources interleave: field 2e = src0[e], field 2e+1 = src1[e]; fields
+      // 0..15 are group a's values, 16..31 group b's.
+      v16f ev, od;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ev[e] = xa[2 * e] * ia;
+        od[e] = xa[2 * e + 1] * ia;
+        ev[8 + e] = xb[2 * e] * ib;
+        od[8 + e] = xb[2 * e + 1] * ib;
+      }
+      const v6i img = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
+      const uint2 qa = fold_fp6((uint32_t)img[0], (uint32_t)img[1], (uint32_t)img[2]);
+      const uint2 qb = fold_fp6((uint32_t)img[3], (uint32_t)img[4], (uint32_t)img[5]);
+      __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)qa.x, (int)qa.y}, qr, (ga * m_pad + row) * 32 + kc * 8, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)qb.x, (int)qb.y}, qr,
+                                            two ? (gb * m_pad + row) * 32 + kc * 8 : OOB, 0, 0);
+      // the four lanes of a row store the same scale
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne(sa), sr, (ga * m_pad + row) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne(sb), sr, two ? (gb * m_pad + row) * 2 : OOB, 0, 0);
+    } else if constexpr (FMT == W4A4_FMT_MXFP4_B32) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {  // both groups computed (b is zeros when missing), stores dropped then
+        const float (&xh)[16] = j ? xb : xa;
+        const int g = ga + j;
+        // the lane's 16 values lie in 32-block kc / 2, shared with lane kc ^ 1
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(xh[e]));
+        amax = max_over_kc_pair(amax);
+        int e8;
+        if (amax == 0.f) {
+          e8 = -127;
+        } else {
+          int ex;
+          const float mant = frexpf(amax, &ex);  // amax = mant * 2^ex, mant in [0.5, 1)
+          e8 = mant <= 0.75f ? ex - 3 : ex - 2;
+          e8 = max(-127, min(127, e8));
+        }
+        // E2M1 nearest-even of X̂ * 2^-e (exact scaling), sign kept for values that round to
+        // zero: v_cvt_scalef32_pk_fp4_f32 with scale 1 puts codes k, k+1 into byte k/2
+        uint32_t word[2] = {0u, 0u};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float z[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) z[e] = ldexpf(xh[8 * h + e], -e8);
+          word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[0], z[1], 1.0f, 0);
+          word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[2], z[3], 1.0f, 1);
+          word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[4], z[5], 1.0f, 2);
+          word[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[h], z[6], z[7], 1.0f, 3);
+        }
+        const bool live = j == 0 || two;
+        __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)word[0], (int)word[1]}, qr,
+                                              live ? (g * m_pad + row) * 32 + kc * 8 : OOB, 0, 0);
+        // lanes kc and kc ^ 1 store the same exponent byte of their block
+        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(e8 + 127), sr,
+                                             live ? (2 * g + (kc >> 1)) * m_pad + row : OOB, 0, 0);
+      }
+    } else {  // W8A8: only the row maximum here; the codes need all of K
+#pragma unroll
+      for (int e = 0; e < 16; ++e) row_amax = fmaxf(row_amax, fmaxf(fabsf(xa[e]), fabsf(xb[e])));
+    }
+    down(xa, i);
+    if (two) down(xb, i + 1);
   }
   if constexpr (FMT == W4A4_FMT_W8A8) {
     // the row's maximum over this slice -> plane sl of the partial maxima behind the scales
-    row_amax = fmaxf(row_amax, __shfl_xor(row_amax, 16));
-    row_amax = fmaxf(row_amax, __shfl_xor(row_amax, 32));
+    row_amax = max_over_kc(row_amax);
     if (kc == 0) static_cast<float*>(xscale)[(size_t)m_pad * (1 + sl) + row] = row_amax;
   }
   if (NT > 0) {
     // 16x16 MFMA output: lane holds rank column c*16 + lane%16, rows 4*(lane/16) + v of the tile
     const size_t n = (size_t)m_pad * RP;
-    float* dst = xl1 + (nsl > 1 ? n * (1 + sl) : 0) + ((size_t)rb * QA_BLOCK_ROWS + wave * 16) * RP;
+    float* dst = xl1 + (nsl > 1 ? n * (1 + sl) : 0) + (size_t)row0 * RP;
 #pragma unroll
     for (int c = 0; c < NT; ++c)
 #pragma unroll
@@ -278,28 +386,29 @@ __global__ __launch_bounds__(QA_WAVES * 64, NT <= 2 ? 4 : 2) void quantize_act_k
 }
 
 // t = Σ_slices partial t, summed in slice order (deterministic); n = m_pad * rank_pad floats.
-// One float4 per thread; the loads of four planes are issued together.
+// One float4 per thread; the loads of up to TR_PLANES planes are issued together (one memory round
+// trip for the usual slice counts).
+constexpr int TR_PLANES = 8;
 __global__ __launch_bounds__(256) void t_reduce_kernel(const float* __restrict__ part, int nsl, int n,
                                                        float* __restrict__ t) {
   const int i = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (i >= n) return;
   auto ld = [&](int k) { return *reinterpret_cast<const float4*>(part + (size_t)k * n + i); };
-  auto add = [](float4& s, const float4& v) {
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
-  };
   float4 s = ld(0);
-  int k = 1;
-  for (; k + 3 < nsl; k += 4) {
-    const float4 a = ld(k), b = ld(k + 1), c = ld(k + 2), d = ld(k + 3);
-    add(s, a);
-    add(s, b);
-    add(s, c);
-    add(s, d);
+  for (int k0 = 1; k0 < nsl; k0 += TR_PLANES) {
+    float4 v[TR_PLANES];
+#pragma unroll
+    for (int k = 0; k < TR_PLANES; ++k)
+      if (k0 + k < nsl) v[k] = ld(k0 + k);
+#pragma unroll
+    for (int k = 0; k < TR_PLANES; ++k)
+      if (k0 + k < nsl) {
+        s.x += v[k].x;
+        s.y += v[k].y;
+        s.z += v[k].z;
+        s.w += v[k].w;
+      }
   }
-  for (; k < nsl; ++k) add(s, ld(k));
   *reinterpret_cast<float4*>(t + i) = s;
 }
 
@@ -1114,7 +1223,7 @@ w4a4_status_t w4a4_quantize_act(const uint16_t* X, int M, int K, int ldx, const 
   w4a4_status_t st = check_shape(M, rank > 0 ? rank : 1, K, rank, fmt);
   if (st != W4A4_OK) return st;
   if (!X || !inv_lambda || !xq || !xscale) return W4A4_ERR_INVALID_ARG;
-  if (ldx < K || ldx % 8 != 0) return W4A4_ERR_INVALID_ARG;
+  if (ldx < K || ldx % 8 != 0 || ldx > QA_MAX_LDX) return W4A4_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(inv_lambda) || !aligned16(xq) || !aligned16(xscale)) return W4A4_ERR_INVALID_ARG;
   if (rank > 0 && (!l1t || !xl1 || !aligned16(l1t) || !aligned16(xl1))) return W4A4_ERR_INVALID_ARG;
   const int m_pad = rows_pad_of(M), nt = rank_pad_of(rank) / 16;
@@ -1157,7 +1266,7 @@ w4a4_status_t w4a4_gelu_quantize_act(const uint16_t* Y, int M, int K, int ldy, c
   w4a4_status_t st = check_shape(M, rank > 0 ? rank : 1, K, rank, fmt);
   if (st != W4A4_OK) return st;
   if (!Y || !inv_lambda || !xq || !xscale) return W4A4_ERR_INVALID_ARG;
-  if (ldy < K || ldy % 8 != 0) return W4A4_ERR_INVALID_ARG;
+  if (ldy < K || ldy % 8 != 0 || ldy > QA_MAX_LDX) return W4A4_ERR_INVALID_ARG;
   if (!aligned16(Y) || !aligned16(inv_lambda) || !aligned16(xq) || !aligned16(xscale)) return W4A4_ERR_INVALID_ARG;
   if (rank > 0 && (!l1t || !xl1 || !aligned16(l1t) || !aligned16(xl1))) return W4A4_ERR_INVALID_ARG;
   const hipError_t e = dispatch_qa<W4A4_FMT_INT4_G64, true>(rank_pad_of(rank) / 16, Y, M, K, ldy, inv_lambda, l1t,

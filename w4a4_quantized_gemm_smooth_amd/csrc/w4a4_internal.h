@@ -38,13 +38,23 @@ inline w4a4_status_t check_shape(int M, int N, int K, int rank, int fmt) {
   return W4A4_OK;
 }
 
-// Activation kernel blocking: 128 rows x a slice of at most QA_MAX_GS groups per block, so the
-// slice's L1 rows are fetched once per 128 rows. With several slices each block writes the
-// partial t of its slice to a scratch plane behind t, and a second kernel sums the planes in slice
-// order (deterministic). Cross-block reduction inside one kernel would need device-scope release
-// fences, which write back the per-XCD L2s.
-constexpr int QA_BLOCK_ROWS = 128, QA_MAX_GS = 8;
-constexpr int QA_TARGET_BLOCKS = 128;  // slices are added until the grid has this many blocks
+// Activation kernel blocking: 64 rows x a slice of at most QA_MAX_GS groups per block, so the
+// slice's L1 rows are fetched once per 64 rows. With several slices each block writes the partial t
+// of its slice to a scratch plane behind t, and a second kernel sums the planes in slice order
+// (deterministic). Cross-block reduction inside one kernel would need device-scope release fences,
+// which write back the per-XCD L2s.
+#ifndef W4A4_QA_BLOCK_ROWS  // build-time tuning knobs (rows per block: a multiple of 16, at most 256)
+#define W4A4_QA_BLOCK_ROWS 64
+#endif
+#ifndef W4A4_QA_MAX_GS
+#define W4A4_QA_MAX_GS 8
+#endif
+#ifndef W4A4_QA_TARGET_BLOCKS
+#define W4A4_QA_TARGET_BLOCKS 256
+#endif
+constexpr int QA_BLOCK_ROWS = W4A4_QA_BLOCK_ROWS, QA_MAX_GS = W4A4_QA_MAX_GS;
+constexpr int QA_TARGET_BLOCKS = W4A4_QA_TARGET_BLOCKS;  // slices are added until the grid has this many blocks
+static_assert(QA_BLOCK_ROWS % 16 == 0 && QA_BLOCK_ROWS <= 256 && QA_MAX_GS % 2 == 0, "activation blocking");
 inline int qa_group_slice(int M, int K) {  // groups per slice
   const int rb = rows_pad_of(M) / QA_BLOCK_ROWS, G = K / W4A4_GROUP;
   int ks = (QA_TARGET_BLOCKS + rb - 1) / rb;
@@ -67,6 +77,10 @@ inline size_t xl1_floats(int M, int K, int rank) {
 // floats of a W8A8 xscale buffer: the [m_pad] per-token scales, then one [m_pad] plane of partial
 // row maxima per slice (written by the first activation kernel, reduced by the second)
 inline size_t w8_xscale_floats(int M, int K) { return size_t(rows_pad_of(M)) * size_t(1 + qa_slices(M, K)); }
+
+// Largest activation row stride (elements) the activation kernel addresses: 16 rows of it must
+// stay below 2^31 bytes (32-bit buffer offsets).
+constexpr int QA_MAX_LDX = 1 << 26;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
