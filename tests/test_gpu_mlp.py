@@ -66,8 +66,10 @@ def _check_fc2_activations(c, y1_bits, a2, rows=None):
     assert np.array_equal(codes, O.pack_int4(act["cx"])), "fc2 activation codes differ"
     assert np.array_equal(scales, O.f32_to_bf16_bits(act["sx"])), "fc2 activation scales differ"
     mp = (m + 255) // 256 * 256
-    xq = a2["xq"].cpu().numpy().reshape(n // 64, mp, 32)
-    assert not xq[:, m:].any(), "padding rows of fc2's codes must be zero"
+    xq = a2["xq"].cpu().numpy()
+    main = xq[: n // 64 * mp * 32].reshape(n // 64, mp, 32)
+    extra = xq[n // 64 * mp * 32:].reshape(n // 64, 2, mp, 8)
+    assert not main[:, m:].any() and not extra[:, :, m:].any(), "padding rows of fc2's codes must be zero"
     if r2:
         rp = (r2 + 15) // 16 * 16
         t = a2["xl1"].cpu().numpy()[: mp * rp].reshape(mp, rp)

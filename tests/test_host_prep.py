@@ -38,7 +38,7 @@ def test_single_hip_runtime_in_process():
 def test_buffer_sizes():
     s = w4.buffer_sizes(4608, 9216, 3072, 32, w4.FMT_INT4_G64)
     assert (s["m_pad"], s["n_pad"], s["rank_pad"]) == (4608, 9216, 32)
-    assert s["wq"] == 9216 * 1536 and s["wscale"] == 48 * 9216 * 2 and s["xl1"] >= 4608 * 32 * 4
+    assert s["wq"] == 9216 * 2304 and s["wscale"] == 48 * 9216 * 2 and s["xl1"] >= 4608 * 32 * 4
     s = w4.buffer_sizes(1000, 300, 128, 20, w4.FMT_MXFP4_B32)
     assert (s["m_pad"], s["n_pad"], s["rank_pad"]) == (1024, 512, 32)
     assert s["wscale"] == 4 * 512 and s["xscale"] == 4 * 1024 and s["l1t"] == 32 * 128 * 2
@@ -117,36 +117,48 @@ def test_weight_codes_bit_exact_given_oracle_factors(shape, fmt):
         assert np.array_equal(l1t[:r].T, l1b) and not l1t[r:].any()
         assert np.array_equal(l2t[:n, :r].T, l2b) and not l2t[:, r:].any() and not l2t[n:].any()
     # padding rows are zero codes with zero scales
-    wq = prep["wq"].reshape(k // (32 if fmt == "w8a8" else 64), prep["n_pad"], 32)
-    assert not wq[:, n:].any()
+    np_ = prep["n_pad"]
+    if fmt == "int4_g64":   # main parts, then the extra parts of both halves
+        main = prep["wq"][: k // 64 * np_ * 32].reshape(k // 64, np_, 32)
+        extra = prep["wq"][k // 64 * np_ * 32:].reshape(k // 64, 2, np_, 8)
+        assert not main[:, n:].any() and not extra[:, :, n:].any()
+    else:
+        wq = prep["wq"].reshape(k // (32 if fmt == "w8a8" else 64), np_, 32)
+        assert not wq[:, n:].any()
 
 
-def _unfold_int4(raw):
-    """Decode the folded INT4 layout of include/w4a4.h: per row, 8 dwords; the pair (d[2j], d[2j+1])
-    holds the FP6 E2M3 image (fields sign<<5 | |q| at bit 6f) of codes 16j..16j+15."""
-    d = raw.reshape(raw.shape[0], 8, 4).astype(np.uint64)
-    d = d[..., 0] | (d[..., 1] << 8) | (d[..., 2] << 16) | (d[..., 3] << 24)
-    out = np.zeros((raw.shape[0], 64), np.int16)
-    for j in range(4):
-        lo, hi = d[:, 2 * j], d[:, 2 * j + 1]
-        img = [lo & 0xE79E79E7, (lo & 0x18618618) | (hi & 0x61861861), hi & 0x9E79E79E]
-        bits = [int(x) for x in img[0]], [int(x) for x in img[1]], [int(x) for x in img[2]]
-        for f in range(16):
-            fld = np.array([((o0 | (o1 << 32) | (o2 << 64)) >> (6 * f)) & 63
-                            for o0, o1, o2 in zip(*bits)], np.int16)
-            assert not (fld & 0b011000).any(), "exponent bits of an FP6 carrier must be zero"
-            out[:, 16 * j + f] = np.where(fld & 32, -(fld & 7), fld & 7)
+def _decode_int4(main, extra0, extra1):
+    """Decode the INT4 layout of include/w4a4.h for rows of one group: the FP6 E2M3 images (fields
+    sign<<5 | |q| at bit 6f) of the four 16-code runs; half h's main part holds dwords d0 d1 d2 of
+    run 2h and d0 of run 2h+1, its extra part d1 d2 of run 2h+1."""
+    dw = lambda a: (a.reshape(a.shape[0], -1, 4).astype(np.uint64) *
+                    (np.uint64(1) << np.arange(0, 32, 8, dtype=np.uint64))).sum(-1)
+    m, x = dw(main), [dw(extra0), dw(extra1)]
+    out = np.zeros((main.shape[0], 64), np.int16)
+    for h in range(2):
+        runs = [m[:, 4 * h: 4 * h + 3], np.stack([m[:, 4 * h + 3], x[h][:, 0], x[h][:, 1]], 1)]
+        for j, run in enumerate(runs):
+            img = [int(a) | (int(b) << 32) | (int(c) << 64) for a, b, c in run]
+            for f in range(16):
+                fld = np.array([(v >> (6 * f)) & 63 for v in img], np.int16)
+                assert not (fld & 0b011000).any(), "exponent bits of an FP6 carrier must be zero"
+                out[:, 32 * h + 16 * j + f] = np.where(fld & 32, -(fld & 7), fld & 7)
+        assert all((v >> 96) == 0 for v in img)
     return out
 
 
 def test_padding_and_layout_of_weight_codes():
-    """Library layout: [G][n_pad][32]; INT4 codes folded FP6 images, MXFP4 plain E2M1 nibbles."""
+    """Library layout: INT4 FP6 images, main parts [G][n_pad][32] then extra parts [G][2][n_pad][8];
+    MXFP4 plain E2M1 nibbles [G][n_pad][32]."""
     d = synth.make_layer(8, 64, 3, n_outliers=1, outlier_scale=10.0, seed=3)
     lam = np.ones(64, np.float32)
     prep = w4.prepare_weights(d["w"], lam, 0, "int4_g64")
     q, s = O.quant_int4_g64(O.bf16_bits_to_f32(d["w"]))
-    raw = prep["wq"].reshape(1, 256, 32)[0, :3]
-    assert np.array_equal(_unfold_int4(raw), q)
+    assert prep["wq"].size == 256 * 48
+    main = prep["wq"][: 256 * 32].reshape(256, 32)
+    extra = prep["wq"][256 * 32:].reshape(2, 256, 8)
+    assert np.array_equal(_decode_int4(main[:3], extra[0, :3], extra[1, :3]), q)
+    assert not main[3:].any() and not extra[:, 3:].any()
     assert (np.abs(q) >= 6).any() and (q < 0).any()      # the case exercises signs and large codes
     prep = w4.prepare_weights(d["w"], lam, 0, "mxfp4_b32")
     qm, _ = O.quant_mxfp4_b32(O.bf16_bits_to_f32(d["w"]))

@@ -36,21 +36,24 @@ using namespace w4a4::dev;
 
 namespace {
 
-// Folded FP6 layout of INT4 codes. A run of 16 codes c_0..c_15 has the FP6 image
-// I = Σ_f (sign_f << 5 | |c_f|) << 6f (96 bits, dwords o0 o1 o2). Bits 3 and 4 of every 6-bit field
-// (the exponent) are zero, which frees exactly the bit positions of the middle dword: stored are
-// lo = (o0 & C0) | (o1 & C34) and hi = (o1 & C05) | (o2 & C2), with masks over p = bit % 6:
-// C0 = {0,1,2,5}, C34 = {3,4}, C05 = {0,5}, C2 = {1,2,3,4}.
-constexpr uint32_t FOLD_C0 = 0xE79E79E7u, FOLD_C34 = 0x18618618u, FOLD_C05 = 0x61861861u, FOLD_C2 = 0x9E79E79Eu;
-
-__device__ __forceinline__ uint2 fold_fp6(uint32_t o0, uint32_t o1, uint32_t o2) {
-  return make_uint2((o0 & FOLD_C0) | (o1 & FOLD_C34), (o1 & FOLD_C05) | (o2 & FOLD_C2));
-}
-
-// 16 B of folded codes (32 codes of one row, one half of a group) -> the 6-dword FP6 operand
-__device__ __forceinline__ v8i unfold_fp6(v4i d) {
-  return v8i{d[0] & (int)FOLD_C0, (d[0] & (int)FOLD_C34) | (d[1] & (int)FOLD_C05), d[1] & (int)FOLD_C2,
-             d[2] & (int)FOLD_C0, (d[2] & (int)FOLD_C34) | (d[3] & (int)FOLD_C05), d[3] & (int)FOLD_C2, 0, 0};
+// INT4 code layout (shared with the host preparation): per row and group the FP6 images of the four
+// 16-code runs (run j = codes 16j .. 16j+15, image dwords d0 d1 d2, field f = sign<<5 | |q| at bit
+// 6f). Half h (runs 2h, 2h+1) is one lane's 6-dword MFMA operand, split into a 16-byte main part
+// [d0 d1 d2 of run 2h, d0 of run 2h+1] at byte (g·rows_pad + row)·32 + 16h and an 8-byte extra part
+// [d1 d2 of run 2h+1] at byte rows_pad·K/2 + ((2g + h)·rows_pad + row)·8 of the code buffer.
+// Byte offsets of run kc's three image dwords (kc = 0..3), for a row of group g:
+__device__ __forceinline__ void int4_run_offsets(int g, int row, int rows_pad, int K, int kc, int (&off)[3]) {
+  const int h = kc >> 1, main = (g * rows_pad + row) * 32 + 16 * h;
+  if ((kc & 1) == 0) {
+    off[0] = main;
+    off[1] = main + 4;
+    off[2] = main + 8;
+  } else {
+    const int extra = rows_pad * (K / 2) + ((2 * g + h) * rows_pad + row) * 8;
+    off[0] = main + 12;
+    off[1] = extra;
+    off[2] = extra + 4;
+  }
 }
 
 // GELU(y) = (y/2)·(1 + erf(y/√2)) in fp32, erf from Abramowitz & Stegun 7.1.28
@@ -82,8 +85,8 @@ __device__ __forceinline__ float gelu32(float y) {
 // product is formed as in the method, and v_cvt_scalef32_2xpk16_fp6_f32 rounds y / 8 to
 // nearest-even on the E2M3 subnormal grid (step 1/8), i.e. emits exactly the carrier field
 // sign|00|rint(y). Its two sources interleave (field 2e = src0[e], field 2e+1 = src1[e]); fields
-// 16..31 are unused. Returns the lane's 16 codes folded into 8 bytes and the scale's bf16 bits.
-__device__ __forceinline__ uint2 quant_int4_lane(const float (&xh)[2][8], uint32_t& s_bits) {
+// 16..31 are unused. Returns the 96-bit image of the lane's 16 codes and the scale's bf16 bits.
+__device__ __forceinline__ uint3 quant_int4_lane(const float (&xh)[2][8], uint32_t& s_bits) {
   float amax = 0.f;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -104,7 +107,7 @@ __device__ __forceinline__ uint2 quant_int4_lane(const float (&xh)[2][8], uint32
   }
   const v6i img = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
   s_bits = bf16_rne(s);
-  return fold_fp6((uint32_t)img[0], (uint32_t)img[1], (uint32_t)img[2]);
+  return make_uint3((uint32_t)img[0], (uint32_t)img[1], (uint32_t)img[2]);
 }
 
 // ===================================================================================
@@ -257,7 +260,8 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
   // the outputs as buffers: a store whose offset lies past the buffer is dropped, so a pair without
   // its second group needs no branch
   const int G2 = FMT == W4A4_FMT_MXFP4_B32 ? 2 * G : G;  // scale planes
-  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(xq, 0, G * m_pad * 32, 0x00020000);
+  const __amdgpu_buffer_rsrc_t qr =
+      __builtin_amdgcn_make_buffer_rsrc(xq, 0, G * m_pad * (FMT == W4A4_FMT_INT4_G64 ? 48 : 32), 0x00020000);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
       xscale, 0, FMT == W4A4_FMT_W8A8 ? 0 : G2 * m_pad * (FMT == W4A4_FMT_INT4_G64 ? 2 : 1), 0x00020000);
 
@@ -315,11 +319,15 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
         od[8 + e] = xb[2 * e + 1] * ib;
       }
       const v6i img = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
-      const uint2 qa = fold_fp6((uint32_t)img[0], (uint32_t)img[1], (uint32_t)img[2]);
-      const uint2 qb = fold_fp6((uint32_t)img[3], (uint32_t)img[4], (uint32_t)img[5]);
-      __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)qa.x, (int)qa.y}, qr, (ga * m_pad + row) * 32 + kc * 8, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)qb.x, (int)qb.y}, qr,
-                                            two ? (gb * m_pad + row) * 32 + kc * 8 : OOB, 0, 0);
+      // the image dwords of this lane's run of each group go straight to the code layout
+      int oa[3], ob[3];
+      int4_run_offsets(ga, row, m_pad, K, kc, oa);
+      int4_run_offsets(gb, row, m_pad, K, kc, ob);
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        __builtin_amdgcn_raw_buffer_store_b32(img[d], qr, oa[d], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(img[3 + d], qr, two ? ob[d] : OOB, 0, 0);
+      }
       // the four lanes of a row store the same scale
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne(sa), sr, (ga * m_pad + row) * 2, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne(sb), sr, two ? (gb * m_pad + row) * 2 : OOB, 0, 0);
@@ -416,29 +424,38 @@ __global__ __launch_bounds__(256) void t_reduce_kernel(const float* __restrict__
 // Kernel 2: the INT4 GEMM + low-rank up projection (+ bias), bf16 out.
 //
 // Block tile 256 (M) x 256 (N), 8 waves as 2 (M) x 4 (N); each wave owns a 4 x 2 grid of 32x32
-// tiles. One K step = one 64-wide group. The codes and scales of each group are copied global ->
-// LDS by the LDS DMA path (global_load_lds) into a ring of I4_NS slots, issued four groups before
-// their first reader; one barrier per two groups publishes the next slots.
-// Per group each wave unfolds its A and B operands to FP6 and runs, per tile, one FP6 MFMA with
-// E8M0 scales 2^3 x 2^3 (the exact integer dot product of the group), one bf16 MFMA (the exact
-// outer product s_x s_w of the raw bf16 scales) and 16 FMAs into its fp32 accumulators.
+// tiles. One K step = one 64-wide group. The codes (FP6 images: a 16-byte main and an 8-byte
+// extra part per row and half) and scales of each group are copied global -> LDS by the LDS DMA
+// path (buffer_load ... lds) into a ring of I4_RING slots, issued four groups before their first
+// reader; one barrier per two groups publishes the next slots. Per group each wave reads its A and
+// B operands as they are (one 16-byte and one 8-byte LDS read each, no unpacking) and runs, per
+// tile, one FP6 MFMA with E8M0 scales 2^3 x 2^3 (the exact integer dot product of the group), one
+// bf16 MFMA (the exact outer product s_x s_w of the raw bf16 scales) and 16 FMAs into its fp32
+// accumulators.
 // The epilogue adds bf16(t)·L2 and the bias and writes Y through LDS in 16-byte row segments.
 // ===================================================================================
 constexpr int I4_THREADS = 512;
 
-// One ring slot: the folded codes of 256 A rows and 256 B rows (32 B each, swizzled) and their
-// bf16 scales (A rows 0..255, then B rows). Each slot is its own LDS object, so the compiler can
-// tell the DMA writes into one slot from the reads of another.
+// One ring slot: the codes of 256 A rows and 256 B rows of one group, main parts (32 B per row,
+// halves swizzled) and extra parts ([half][row][8 B]), and their bf16 scales (A rows 0..255, then
+// B rows). Each slot is its own LDS object, so the compiler can tell the DMA writes into one slot
+// from the reads of another. Six slots (150 KB) fill the CU's LDS.
+constexpr int I4_RING = 6;  // even: one barrier per two groups
 struct I4Slot {
   uint8_t a[256 * 32];
   uint8_t b[256 * 32];
+  uint8_t ax[2 * 256 * 8];
+  uint8_t bx[2 * 256 * 8];
   uint16_t s[512];
   uint16_t z[32];  // zeros (never written by the DMA): k > 0 half of the scale outer-product operand
 };
+// After the main loop every wave stages its output through half a slot (wave w: slot w / 2)
+constexpr int I4_STAGE = 12800;
+static_assert(2 * I4_STAGE <= (int)sizeof(I4Slot) && I4_THREADS / 64 <= 2 * I4_RING, "staging areas");
 
 // The next layer's activation side in this GEMM's epilogue (the MLP's fc1 -> GELU -> fc2 join):
 // fc2's 1/λ over this layer's N columns, fc2's L1ᵀ [rank2_pad][N], and fc2's outputs in library
-// layout: INT4 codes [N/64][m_pad][32 B], bf16 scales [N/64][m_pad], and one partial t plane
+// layout: INT4 codes (FP6 images of K = N), bf16 scales [N/64][m_pad], and one partial t plane
 // [m_pad][rank2_pad] per 256-column tile of this layer.
 struct GeluQuantArgs {
   const float* il2;
@@ -448,9 +465,9 @@ struct GeluQuantArgs {
   float* t2part;
 };
 
-// the block's eight ring slots, by value (indexed with constants only, so they stay in registers)
+// the eight waves' staging areas, by value (indexed with constants only, so they stay in registers)
 struct SlotSet {
-  uint8_t* s[I4_NS];
+  uint8_t* s[8];
 };
 
 template <int NT2>
@@ -468,8 +485,9 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int M, int N, int K,
     int m_pad, int n_pad, GeluQuantArgs fa) {
   static_assert(FMT == W4A4_FMT_INT4_G64, "MXFP4 runs on gemm_mx_small_kernel and gemm_w8a8_kernel<., true>");
-  __shared__ __attribute__((aligned(16))) I4Slot sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7;
-  I4Slot* const ring[I4_NS] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5, &sl6, &sl7};
+  static_assert(I4_RING == 6, "six ring objects");
+  __shared__ __attribute__((aligned(16))) I4Slot sl0, sl1, sl2, sl3, sl4, sl5;
+  I4Slot* const ring[I4_RING] = {&sl0, &sl1, &sl2, &sl3, &sl4, &sl5};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps derived addresses scalar
@@ -479,11 +497,13 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   const int m0 = tm * I4_BM, n0 = tn * I4_BN;
   const int G = K / W4A4_GROUP;
 
-  // ---- DMA sources. Instruction w of an operand fills LDS bytes [1024 w, 1024 w + 1024) of the
+  // ---- DMA sources. Instruction w of an operand's main parts fills LDS bytes [1024 w, +1024) of the
   // slot, lane i the 16 bytes at 1024 w + 16 i = row 32 w + i / 2, stored half i & 1; the lane
-  // loads the global half that the swizzle puts there. Scales: wave w copies 256 bytes, chunk
-  // w & 3 of the slot's 1 KB of scales (waves w and w + 4 write the same bytes): the bf16 scales
-  // of A rows 0..127, A rows 128..255, B rows 0..127, B rows 128..255.
+  // loads the global half that the swizzle puts there. Extra parts: wave w < 4 copies quarter w of
+  // A's 4 KB ([half][row][8 B]: half w / 2, rows 128 (w & 1) ..), wave w >= 4 quarter w - 4 of B's.
+  // Scales: wave w copies 256 bytes, chunk w & 3 of the slot's 1 KB of scales (waves w and w + 4
+  // write the same bytes): the bf16 scales of A rows 0..127, A rows 128..255, B rows 0..127,
+  // B rows 128..255.
   const int drow = 32 * wave + (lane >> 1);
   const int dhalf = (lane & 1) ^ ((drow >> 3) & 1);
   const int c_lane = drow * 32 + 16 * dhalf;   // byte offset of the lane's 16 B in a code tile
@@ -496,6 +516,13 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
       const_cast<uint8_t*>(xq + (size_t)m0 * 32), 0, (G * m_pad - m0) * 32, RSRC_W3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(wq + (size_t)n0 * 32), 0, (G * n_pad - n0) * 32, RSRC_W3);
+  // extra parts: planes [2 G][rows_pad][8 B] behind the main planes
+  const bool x_is_a = wave < 4;
+  const int x_rows = x_is_a ? m_pad : n_pad, x_row0 = x_is_a ? m0 : n0, xq4 = wave & 3;
+  const uint8_t* x_buf = (x_is_a ? xq : wq) + (size_t)x_rows * (K / 2);
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(x_buf + (size_t)x_row0 * 8), 0, (2 * G * x_rows - x_row0) * 8, RSRC_W3);
+  const int x_lane = (xq4 >> 1) * x_rows * 8 + (xq4 & 1) * 1024 + 16 * lane;  // half, row block, lane
   // scale chunk of this wave: bf16 rows [128 c, 128 c + 128) of A (c = sblk) or B (c = sblk - 2)
   const bool s_is_a = sblk < 2;
   const int s_rows = s_is_a ? m_pad : n_pad, s_row0 = s_is_a ? m0 : n0, sc_ = s_is_a ? sblk : sblk - 2;
@@ -506,22 +533,24 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(s_buf + s_first), 0, s_total - s_first, RSRC_W3);
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  // 3 vector-memory instructions per wave and group (part 0: A codes, 1: B codes, 2: scales);
-  // groups past the end reload the last group
+  // 4 vector-memory instructions per wave and group (part 0: A main parts, 1: B main parts,
+  // 2: scales, 3: extra parts); groups past the end reload the last group
+  constexpr int DMA_PER_GROUP = 4;
   auto dma_part = [&](int part, int g, I4Slot* sl) {
     g = min(g, G - 1);
     if (part == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr)(sl->a + 1024 * wave), 16, c_lane, g * m_pad * 32, 0, 0);
     else if (part == 1)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr)(sl->b + 1024 * wave), 16, c_lane, g * n_pad * 32, 0, 0);
-    else
+    else if (part == 2)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr)(sl->s + 128 * sblk), 4, s_lane, g * s_gstride, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lds_ptr)((x_is_a ? sl->ax : sl->bx) + 1024 * xq4), 16, x_lane,
+                                               g * 2 * x_rows * 8, 0, 0);
   };
   auto dma = [&](int g, I4Slot* sl) {
-    g = min(g, G - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr)(sl->a + 1024 * wave), 16, c_lane, g * m_pad * 32, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr)(sl->b + 1024 * wave), 16, c_lane, g * n_pad * 32, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr)(sl->s + 128 * sblk), 4, s_lane, g * s_gstride, 0, 0);
+#pragma unroll
+    for (int part = 0; part < DMA_PER_GROUP; ++part) dma_part(part, g, sl);
   };
 
   v16f acc[I4_MT][2];
@@ -539,20 +568,20 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
 
   // low-rank up projection first: acc = bf16(t) · L2 over k = rank index (32x32x16 bf16 MFMA); the
   // 4-bit groups then accumulate on top. Up to rank 32 the block's t tile (256 rows x 32 fp32 =
-  // 32 KB, read by four waves each) is copied once into ring slots 6 and 7 by the LDS DMA path
+  // 32 KB, read by four waves each) is copied once into the last two ring slots by the LDS DMA path
   // before the ring's first groups, and the L2 operands are loaded before them too; all of it
   // lands under the prologue's wait for group 0 and the MFMAs run right after it. Larger ranks
   // load t directly, 32 ranks at a time.
   constexpr int RP = NTR * 16, KS = 2;  // up to two 16-rank MFMA K-steps per batch of loads
   constexpr bool T_LDS = NTR > 0 && NTR <= 2;
   constexpr int TROWB = RP * 4;          // bytes of one t row
-  static_assert(256 * 32 * 4 <= 2 * 16384 && 16384 <= (int)sizeof(I4Slot), "t tile fits slots 6 and 7");
+  static_assert(256 * 32 * 4 <= 2 * 16384 && 16384 <= (int)sizeof(I4Slot), "t tile fits the last two slots");
   // t row r of the block lives at byte r * TROWB of the tile: the first 16 KB in slot 6, the rest
   // in slot 7
   auto t_row_ptr = [&](int r) -> const uint8_t* {
     const int byte = r * TROWB;
-    return byte < 16384 ? reinterpret_cast<const uint8_t*>(ring[6]) + byte
-                        : reinterpret_cast<const uint8_t*>(ring[7]) + (byte - 16384);
+    return byte < 16384 ? reinterpret_cast<const uint8_t*>(ring[I4_RING - 2]) + byte
+                        : reinterpret_cast<const uint8_t*>(ring[I4_RING - 1]) + (byte - 16384);
   };
   v4i LB[KS][2];
   float4 tv[KS][I4_MT][2];
@@ -630,7 +659,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     }
   };
   if (NTR > 0) lr_load(0);
-  if (T_LDS) {  // t tile -> slots 6 and 7: TBYTES / 8 bytes per wave, 1 KB per DMA instruction
+  if (T_LDS) {  // t tile -> the last two slots: TBYTES / 8 bytes per wave, 1 KB per DMA instruction
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     const __amdgpu_buffer_rsrc_t t_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(xl1 + (size_t)m0 * RP), 0, (m_pad - m0) * TROWB, RSRC_W3);
@@ -638,8 +667,8 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
 #pragma unroll
     for (int q = 0; q < TCHUNK / 1024; ++q) {
       const int off = wave * TCHUNK + q * 1024;  // chunks never straddle the 16 KB split
-      uint8_t* dst = off < 16384 ? reinterpret_cast<uint8_t*>(ring[6]) + off
-                                 : reinterpret_cast<uint8_t*>(ring[7]) + (off - 16384);
+      uint8_t* dst = off < 16384 ? reinterpret_cast<uint8_t*>(ring[I4_RING - 2]) + off
+                                 : reinterpret_cast<uint8_t*>(ring[I4_RING - 1]) + (off - 16384);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr_t)dst, 16, 16 * lane, off, 0, 0);
     }
   }
@@ -647,11 +676,11 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   // prologue: zero words of every slot; groups 0 .. NS-3 in flight; group 0 visible
   if (tid < 32) {
 #pragma unroll
-    for (int s = 0; s < I4_NS; ++s) ring[s]->z[tid] = 0;
+    for (int s = 0; s < I4_RING; ++s) ring[s]->z[tid] = 0;
   }
 #pragma unroll
-  for (int s = 0; s < I4_NS - 2; ++s) dma(s, ring[s]);
-  wait_vmcnt<3 * (I4_NS - 3)>();
+  for (int s = 0; s < I4_RING - 2; ++s) dma(s, ring[s]);
+  wait_vmcnt<DMA_PER_GROUP * (I4_RING - 3)>();
   __builtin_amdgcn_s_barrier();
   if (NTR > 0) {
     if (T_LDS) t_from_lds();
@@ -662,8 +691,16 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
       lr_mfma(k0);
     }
   }
-  auto a_raw = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off + 1024 * i); };
-  auto b_raw = [&](const I4Slot* sl, int j) { return *reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j); };
+  // an operand as it sits in LDS: the 16-byte main part and the 8-byte extra part of the lane's half
+  struct Raw {
+    v4i m;
+    v2i x;
+  };
+  auto op6 = [](const Raw& r) { return v8i{r.m[0], r.m[1], r.m[2], r.m[3], r.x[0], r.x[1], 0, 0}; };
+  const int bx_off = lh * 2048 + bcol0 * 8;
+  auto b_raw = [&](const I4Slot* sl, int j) {
+    return Raw{*reinterpret_cast<const v4i*>(sl->b + b_off + 1024 * j), *reinterpret_cast<const v2i*>(sl->bx + bx_off + 256 * j)};
+  };
   // Row rotation against VGPR bank conflicts. The FMA acc[v] += p[v] * sc[v] would read three
   // registers with the same index in three tuples that the allocator places at the same alignment,
   // i.e. three times the same bank. Instead the lane that supplies A row rho of the FP6 MFMA loads
@@ -676,8 +713,11 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     return ((u >> 2) << 3) | (rho & 4) | (u & 3);
   };
   const int a_off4 = sw_off32(wm * 128 + rot(lr, 2), lh);
+  const int ax_off4 = lh * 2048 + (wm * 128 + rot(lr, 2)) * 8;
   const int srow0 = wm * 128 + rot(lr, 1);
-  auto a_raw4 = [&](const I4Slot* sl, int i) { return *reinterpret_cast<const v4i*>(sl->a + a_off4 + 1024 * i); };
+  auto a_raw4 = [&](const I4Slot* sl, int i) {
+    return Raw{*reinterpret_cast<const v4i*>(sl->a + a_off4 + 1024 * i), *reinterpret_cast<const v2i*>(sl->ax + ax_off4 + 256 * i)};
+  };
   // operands of the scale outer product: the A side is the bf16 scale of the lane's (rotated) row
   // in every lane; the B side is the scale at k = 0 (lanes 0..31) and zero for k = 4 (lanes
   // 32..63, read from the slot's zero words), and zero for groups past the end, so S = s_x s_w
@@ -694,14 +734,14 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   // its first operands in registers
   v8i Bv[2], Av;
   uint32_t OB[2], OA;
-  v4i An_raw, Bn_raw[2];
+  Raw An_raw, Bn_raw[2];
   uint32_t OAn, OBn[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    Bv[j] = unfold_fp6(b_raw(ring[0], j));
+    Bv[j] = op6(b_raw(ring[0], j));
     OB[j] = sb_val(ring[0], j, true);
   }
-  Av = unfold_fp6(a_raw4(ring[0], 0));
+  Av = op6(a_raw4(ring[0], 0));
   OA = sa_val(ring[0], srow0);
   An_raw = a_raw4(ring[0], 1);
   OAn = sa_val(ring[0], srow0 + 32);
@@ -710,17 +750,17 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Av, Bv[0], zero16, 2, 2, 0, 130, 0, 130);
   v16f sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sc_op(OA), sc_op(OB[0]), zero16, 0, 0, 0);
 
-  for (int g0 = 0; g0 < G; g0 += I4_NS) {
+  for (int g0 = 0; g0 < G; g0 += I4_RING) {
 #pragma unroll
-    for (int u = 0; u < I4_NS; ++u) {
+    for (int u = 0; u < I4_RING; ++u) {
       const int g = g0 + u;
       const I4Slot* cur = ring[u];
-      const I4Slot* nxt = ring[(u + 1) % I4_NS];
+      const I4Slot* nxt = ring[(u + 1) % I4_RING];
       if (u % 2 == 0) {
         // groups g+1 and g+2 have landed in every wave's share of their slots; everyone is done
         // with slots g-2 and g-1, which take groups g+NS-2 (copied during this group) and g+NS-1
         // (during the next)
-        wait_vmcnt<3 * (I4_NS - 5)>();
+        wait_vmcnt<DMA_PER_GROUP * (I4_RING - 5)>();
         __builtin_amdgcn_s_barrier();
       }
       const bool live1 = g + 1 < G;
@@ -736,12 +776,12 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
         if (t1 == T) {  // switch to group g + 1
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
-            Bv[jj] = unfold_fp6(Bn_raw[jj]);
+            Bv[jj] = op6(Bn_raw[jj]);
             OB[jj] = OBn[jj];
           }
         }
         if (j1 == 0) {  // new tile row: take the prefetched A operand
-          Av = unfold_fp6(An_raw);
+          Av = op6(An_raw);
           OA = OAn;
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -762,10 +802,10 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
             OBn[jj] = sb_val(nxt, jj, live1);
           }
         }
-        // this group's copy of group g + NS - 2 into the slot freed at the last barrier, one
+        // this group's copy of group g + I4_RING - 2 into the slot freed at the last barrier, one
         // instruction every other tile (issued together right after the barrier, the copies of all
         // eight waves queue up at once and stall their issue: measured 5-7% slower)
-        if (t == 1 || t == 3 || t == 5) dma_part(t >> 1, g + I4_NS - 2, ring[(u + I4_NS - 2) % I4_NS]);
+        if (t & 1) dma_part(t >> 1, g + I4_RING - 2, ring[(u + I4_RING - 2) % I4_RING]);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch reads here, two tiles ahead of their use
         // raised wave priority around each MFMA issue keeps the matrix pipe fed while the other
         // wave of the SIMD is in its FMAs
@@ -785,19 +825,19 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   }
   wait_vmcnt<0>();  // no LDS DMA may outlive the block
   __builtin_amdgcn_s_barrier();  // every wave is done with the ring (and its DMA has landed)
-  uint8_t* stage = reinterpret_cast<uint8_t*>(ring[0]);
+  // the eight waves' staging areas: wave w uses half (w & 1) of slot w / 2
+  SlotSet slots;
 #pragma unroll
-  for (int w = 1; w < I4_NS; ++w)
-    if (wave == w) stage = reinterpret_cast<uint8_t*>(ring[w]);  // wave-uniform select
-  static_assert(64 * Y_ES <= (int)sizeof(I4Slot), "staging fits a ring slot");
+  for (int w = 0; w < 8; ++w) slots.s[w] = reinterpret_cast<uint8_t*>(ring[w >> 1]) + (w & 1) * I4_STAGE;
+  uint8_t* stage = slots.s[0];
+#pragma unroll
+  for (int w = 1; w < 8; ++w)
+    if (wave == w) stage = slots.s[w];  // wave-uniform select
+  static_assert(64 * Y_ES <= I4_STAGE, "staging fits half a ring slot");
   if constexpr (FUSE < 0) {
     store_y(acc, stage, bias, Y, ldy, M, N, m0 + wm * 128, n0 + wn * 64, lane);
   } else {
     if (Y) store_y(acc, stage, bias, Y, ldy, M, N, m0 + wm * 128, n0 + wn * 64, lane);  // for checking
-    const SlotSet slots{{reinterpret_cast<uint8_t*>(&sl0), reinterpret_cast<uint8_t*>(&sl1),
-                         reinterpret_cast<uint8_t*>(&sl2), reinterpret_cast<uint8_t*>(&sl3),
-                         reinterpret_cast<uint8_t*>(&sl4), reinterpret_cast<uint8_t*>(&sl5),
-                         reinterpret_cast<uint8_t*>(&sl6), reinterpret_cast<uint8_t*>(&sl7)}};
     gelu_quant_epilogue<FUSE>(acc, stage, slots, fa, bias, M, N, m_pad, m0, n0, tn, wm, wn, wave, lane);
   }
 }
@@ -878,9 +918,13 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
         xh[e >> 3][e & 7] = bf16f(bits) * il[e];  // X̂₂, one fp32 multiply
       }
       uint32_t sb;
-      const uint2 q = quant_int4_lane(xh, sb);
+      const uint3 q = quant_int4_lane(xh, sb);
       if (gvalid) {
-        *reinterpret_cast<uint2*>(fa.xq2 + ((size_t)g2 * m_pad + row) * 32 + kc * 8) = q;
+        int off[3];
+        int4_run_offsets(g2, row, m_pad, N, kc, off);
+        reinterpret_cast<uint32_t*>(fa.xq2 + off[0])[0] = q.x;
+        reinterpret_cast<uint32_t*>(fa.xq2 + off[1])[0] = q.y;
+        reinterpret_cast<uint32_t*>(fa.xq2 + off[2])[0] = q.z;
         if (kc == 0) fa.xs2[(size_t)g2 * m_pad + row] = (uint16_t)sb;
       }
       if constexpr (NT2 > 0) {
@@ -898,34 +942,39 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
     }
   }
   if constexpr (NT2 > 0) {
-    // 16x16 MFMA output: lane holds rank column c*16 + lane%16, rows 4*(lane/16) + v of its pass
-    __builtin_amdgcn_s_barrier();  // every wave is done with its staging slot
-    float* mine = reinterpret_cast<float*>(stage);  // the wave's own slot
-    static_assert(128 * RP2 * 4 <= (int)sizeof(I4Slot), "a wave's partial t fits its ring slot");
-#pragma unroll
-    for (int p = 0; p < 8; ++p)
-#pragma unroll
-      for (int c = 0; c < NT2; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) mine[(p * 16 + 4 * kc + v) * RP2 + c * 16 + r] = tacc[p][c][v];
-    __builtin_amdgcn_s_barrier();
+    // 16x16 MFMA output: lane holds rank column c*16 + lane%16, rows 4*(lane/16) + v of its pass.
+    // The partials go through the waves' staging areas 64 rows (of each wave's 128) at a time.
+    float* mine = reinterpret_cast<float*>(stage);
+    static_assert(64 * RP2 * 4 <= I4_STAGE, "64 rows of a wave's partial t fit its staging area");
     const int tid = wave * 64 + lane;
     constexpr int Q = RP2 / 4;  // float4 per row
 #pragma unroll
-    for (int idx0 = 0; idx0 < 256 * Q; idx0 += I4_THREADS) {
-      const int idx = idx0 + tid, row = idx / Q, q = idx % Q;
-      const int wr = row >> 7, lrow = row & 127;
-      float4 sum = float4{0.f, 0.f, 0.f, 0.f};
+    for (int hp = 0; hp < 2; ++hp) {
+      __builtin_amdgcn_s_barrier();  // every wave is done with the staging areas
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {  // the four column waves of these rows, in order
-        const float* src = reinterpret_cast<const float*>(wr ? slots.s[4 + w] : slots.s[w]);
-        const float4 v = *reinterpret_cast<const float4*>(src + lrow * RP2 + 4 * q);
-        sum.x += v.x;
-        sum.y += v.y;
-        sum.z += v.z;
-        sum.w += v.w;
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int c = 0; c < NT2; ++c)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mine[(p * 16 + 4 * kc + v) * RP2 + c * 16 + r] = tacc[4 * hp + p][c][v];
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int idx0 = 0; idx0 < 128 * Q; idx0 += I4_THREADS) {
+        const int idx = idx0 + tid, row = idx / Q, q = idx % Q;
+        const int wr = row >> 6, lrow = row & 63;
+        float4 sum = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {  // the four column waves of these rows, in order
+          const float* src = reinterpret_cast<const float*>(slots.s[4 * wr + w]);
+          const float4 v = *reinterpret_cast<const float4*>(src + lrow * RP2 + 4 * q);
+          sum.x += v.x;
+          sum.y += v.y;
+          sum.z += v.z;
+          sum.w += v.w;
+        }
+        const int brow = wr * 128 + hp * 64 + lrow;  // row within the block
+        *reinterpret_cast<float4*>(fa.t2part + ((size_t)tn * m_pad + m0 + brow) * RP2 + 4 * q) = sum;
       }
-      *reinterpret_cast<float4*>(fa.t2part + ((size_t)tn * m_pad + m0 + row) * RP2 + 4 * q) = sum;
     }
   }
 }

@@ -98,52 +98,70 @@ bool all_finite_bf16(const uint16_t* a, size_t rows, size_t cols, size_t ld) {
 }
 
 // ------------------------------------------------------------------------------ code layouts
-// INT4 codes are stored folded (the layout the GEMM unfolds into FP6 MFMA operands): per row and
-// group 32 bytes = 8 little-endian dwords; dwords 2j and 2j+1 hold codes 16j .. 16j+15 of the
-// group. With F_f = (sign << 5) | |q| (the E2M3 subnormal carrying q / 8) for code 16j + f, the
-// 96-bit image I = Σ_f F_f << 6f has dwords o0 o1 o2, and the pair is
-// lo = (o0 & C0) | (o1 & C34), hi = (o1 & C05) | (o2 & C2) (masks over bit % 6: C0 = {0,1,2,5},
-// C34 = {3,4}, C05 = {0,5}, C2 = {1,2,3,4}).
-constexpr uint32_t kFoldC0 = 0xE79E79E7u, kFoldC34 = 0x18618618u, kFoldC05 = 0x61861861u, kFoldC2 = 0x9E79E79Eu;
+// INT4 codes are stored as their FP6 image, the GEMM's MFMA operands as they are (no unpacking on
+// the device). Per row and group the 64 codes form four runs of 16 (run j = codes 16j .. 16j+15);
+// with F_f = (sign << 5) | |q| (the E2M3 subnormal carrying q / 8) for code 16j + f, a run's image
+// I_j = Σ_f F_f << 6f is 96 bits, little-endian dwords d0 d1 d2. Half h (runs 2h, 2h+1: one lane's
+// 6-dword MFMA operand) is split into a 16-byte main part [d0 d1 d2 of run 2h, d0 of run 2h+1] at
+// main[(g·rows_pad + row)·32 + 16h] and an 8-byte extra part [d1 d2 of run 2h+1] at
+// extra[((2g + h)·rows_pad + row)·8]; the extra planes follow the main planes in the buffer.
+inline size_t int4_extra_offset(int rows_pad, int K) { return size_t(rows_pad) * size_t(K) / 2; }
 
-// nib: 64 sign-magnitude codes (bit 3 = sign) -> 32 folded bytes
-void fold_int4_group(const uint8_t* nib, uint8_t* out32) {
-  for (int j = 0; j < 4; ++j) {
-    uint32_t img[3] = {0, 0, 0};
-    for (int f = 0; f < 16; ++f) {
-      const uint8_t c = nib[16 * j + f];
-      const uint64_t fld = uint64_t(((c & 8u) << 2) | (c & 7u));
-      const int bit = 6 * f;
-      const uint64_t w = fld << (bit & 31);
-      img[bit >> 5] |= uint32_t(w);
-      if ((bit >> 5) + 1 < 3) img[(bit >> 5) + 1] |= uint32_t(w >> 32);
-    }
-    const uint32_t lo = (img[0] & kFoldC0) | (img[1] & kFoldC34);
-    const uint32_t hi = (img[1] & kFoldC05) | (img[2] & kFoldC2);
-    for (int b = 0; b < 4; ++b) {
-      out32[8 * j + b] = uint8_t(lo >> (8 * b));
-      out32[8 * j + 4 + b] = uint8_t(hi >> (8 * b));
-    }
+// the 96-bit image of 16 sign-magnitude codes (bit 3 = sign)
+void fp6_image(const uint8_t* nib16, uint32_t (&img)[3]) {
+  img[0] = img[1] = img[2] = 0;
+  for (int f = 0; f < 16; ++f) {
+    const uint64_t fld = uint64_t(((nib16[f] & 8u) << 2) | (nib16[f] & 7u));
+    const int bit = 6 * f;
+    const uint64_t w = fld << (bit & 31);
+    img[bit >> 5] |= uint32_t(w);
+    if ((bit >> 5) + 1 < 3) img[(bit >> 5) + 1] |= uint32_t(w >> 32);
   }
 }
 
-// 32 folded bytes -> 64 codes as signed values
-void unfold_int4_group(const uint8_t* in32, int* q) {
-  for (int j = 0; j < 4; ++j) {
-    uint32_t lo = 0, hi = 0;
-    for (int b = 0; b < 4; ++b) {
-      lo |= uint32_t(in32[8 * j + b]) << (8 * b);
-      hi |= uint32_t(in32[8 * j + 4 + b]) << (8 * b);
-    }
-    const uint32_t img[3] = {lo & kFoldC0, (lo & kFoldC34) | (hi & kFoldC05), hi & kFoldC2};
-    for (int f = 0; f < 16; ++f) {
-      const int bit = 6 * f;
-      uint64_t w = img[bit >> 5];
-      if ((bit >> 5) + 1 < 3) w |= uint64_t(img[(bit >> 5) + 1]) << 32;
-      const uint32_t fld = uint32_t(w >> (bit & 31)) & 63u;
-      const int mag = int(fld & 7u);
-      q[16 * j + f] = (fld & 32u) ? -mag : mag;
-    }
+inline void put_u32(uint8_t* p, uint32_t v) {
+  for (int b = 0; b < 4; ++b) p[b] = uint8_t(v >> (8 * b));
+}
+inline uint32_t get_u32(const uint8_t* p) {
+  uint32_t v = 0;
+  for (int b = 0; b < 4; ++b) v |= uint32_t(p[b]) << (8 * b);
+  return v;
+}
+
+// nib: 64 sign-magnitude codes of one (row, group) -> its main part (32 bytes) and the extra parts
+// of its two halves (8 bytes each)
+void put_int4_group(const uint8_t* nib, uint8_t* main32, uint8_t* extra0, uint8_t* extra1) {
+  for (int h = 0; h < 2; ++h) {
+    uint32_t a[3], b[3];
+    fp6_image(nib + 32 * h, a);
+    fp6_image(nib + 32 * h + 16, b);
+    uint8_t* m = main32 + 16 * h;
+    put_u32(m, a[0]);
+    put_u32(m + 4, a[1]);
+    put_u32(m + 8, a[2]);
+    put_u32(m + 12, b[0]);
+    uint8_t* x = h ? extra1 : extra0;
+    put_u32(x, b[1]);
+    put_u32(x + 4, b[2]);
+  }
+}
+
+// the inverse: 64 codes as signed values
+void get_int4_group(const uint8_t* main32, const uint8_t* extra0, const uint8_t* extra1, int* q) {
+  for (int h = 0; h < 2; ++h) {
+    const uint8_t* m = main32 + 16 * h;
+    const uint8_t* x = h ? extra1 : extra0;
+    const uint32_t run[2][3] = {{get_u32(m), get_u32(m + 4), get_u32(m + 8)},
+                                {get_u32(m + 12), get_u32(x), get_u32(x + 4)}};
+    for (int j = 0; j < 2; ++j)
+      for (int f = 0; f < 16; ++f) {
+        const int bit = 6 * f;
+        uint64_t w = run[j][bit >> 5];
+        if ((bit >> 5) + 1 < 3) w |= uint64_t(run[j][(bit >> 5) + 1]) << 32;
+        const uint32_t fld = uint32_t(w >> (bit & 31)) & 63u;
+        const int mag = int(fld & 7u);
+        q[32 * h + 16 * j + f] = (fld & 32u) ? -mag : mag;
+      }
   }
 }
 
@@ -151,7 +169,7 @@ void unfold_int4_group(const uint8_t* in32, int* q) {
 // One INT4 group (64 values): s = bf16(max|v| / 7); q = clamp(rint(v * (1/s))); a scale below
 // 2^-126 is stored as 0 with zero codes. Symmetric scaling bounds |v * (1/s)| by
 // 7 / (1 - 2^-8) * (1 + 2^-23)^2 < 7.5, so |q| <= 7 and the sign-magnitude nibble is exact.
-void quant_int4_group(const float* v, uint8_t* out32, uint16_t* scale_bits) {
+void quant_int4_group(const float* v, uint8_t* main32, uint8_t* extra0, uint8_t* extra1, uint16_t* scale_bits) {
   float amax = 0.0f;
   for (int k = 0; k < W4A4_GROUP; ++k) amax = std::max(amax, std::fabs(v[k]));
   float s = bf16_round(amax / 7.0f);
@@ -167,7 +185,7 @@ void quant_int4_group(const float* v, uint8_t* out32, uint16_t* scale_bits) {
       nib[k] = uint8_t((q < 0 ? 8 : 0) | (q < 0 ? -q : q));
     }
   }
-  fold_int4_group(nib, out32);
+  put_int4_group(nib, main32, extra0, extra1);
 }
 
 // e = the smallest integer with 6 * 2^e >= amax, in [-127, 127]; -127 for amax == 0.
@@ -429,7 +447,7 @@ bool split_once(const std::vector<double>& what, const double* target, int N, in
   for (size_t i = 0; i < L2.size(); ++i) l2d[i] = bf16_to_f32(L2[i]);
   // residual and its quantization, one weight row per task
   const bool mx = fmt == W4A4_FMT_MXFP4_B32, w8 = fmt == W4A4_FMT_W8A8;
-  std::memset(wq, 0, w8 ? size_t(np) * K : size_t(np) * K / 2);
+  std::memset(wq, 0, w8 ? size_t(np) * K : mx ? size_t(np) * K / 2 : size_t(np) * K * 3 / 4);
   std::memset(wscale, 0, w8 ? size_t(np) * 4 : mx ? size_t(K / W4A4_MX_BLOCK) * np : size_t(G) * np * 2);
   if (deq) deq->assign(size_t(N) * K, 0.0);
   std::vector<double> row_err(static_cast<size_t>(N), 0.0);
@@ -473,9 +491,11 @@ bool split_once(const std::vector<double>& what, const double* target, int N, in
           }
         } else {
           uint16_t* sb = &static_cast<uint16_t*>(wscale)[size_t(g) * np + n];
-          quant_int4_group(rrow.data() + size_t(g) * W4A4_GROUP, dst, sb);
+          uint8_t* x0 = wq + int4_extra_offset(np, K) + (size_t(2 * g) * np + n) * 8;
+          uint8_t* x1 = wq + int4_extra_offset(np, K) + (size_t(2 * g + 1) * np + n) * 8;
+          quant_int4_group(rrow.data() + size_t(g) * W4A4_GROUP, dst, x0, x1, sb);
           int q[W4A4_GROUP];
-          unfold_int4_group(dst, q);
+          get_int4_group(dst, x0, x1, q);
           const double sc = bf16_to_f32(*sb);
           for (int k = 0; k < W4A4_GROUP; ++k) v[k] = double(q[k]) * sc;
         }
@@ -577,11 +597,11 @@ w4a4_status_t w4a4_buffer_sizes(int M, int N, int K, int rank, int fmt, w4a4_siz
   out->n_pad = int(np);
   out->rank_pad = int(rp);
   const bool w8 = fmt == W4A4_FMT_W8A8;
-  out->wq = w8 ? np * kk : np * kk / 2;
+  out->wq = w8 ? np * kk : mx ? np * kk / 2 : np * kk * 3 / 4;
   out->wscale = w8 ? np * 4 : mx ? (kk / W4A4_MX_BLOCK) * np : (kk / W4A4_GROUP) * np * 2;
   out->l1t = rp * kk * 2;
   out->l2t = np * rp * 2;
-  out->xq = w8 ? mp * kk : mp * kk / 2;
+  out->xq = w8 ? mp * kk : mx ? mp * kk / 2 : mp * kk * 3 / 4;
   out->xscale = w8 ? w8_xscale_floats(M, K) * 4 : mx ? (kk / W4A4_MX_BLOCK) * mp : (kk / W4A4_GROUP) * mp * 2;
   out->xl1 = xl1_floats(M, K, rank) * 4;
   return W4A4_OK;
@@ -660,7 +680,7 @@ w4a4_status_t w4a4_prepare_weights_refined(const uint16_t* W, int N, int K, cons
   return guarded([&] {
     const int np = rows_pad_of(N), G = K / W4A4_GROUP;
     const bool mx = fmt == W4A4_FMT_MXFP4_B32, w8 = fmt == W4A4_FMT_W8A8;
-    const size_t q_bytes = w8 ? size_t(np) * K : size_t(np) * K / 2;
+    const size_t q_bytes = w8 ? size_t(np) * K : mx ? size_t(np) * K / 2 : size_t(np) * K * 3 / 4;
     const size_t s_bytes = w8 ? size_t(np) * 4 : mx ? size_t(K / W4A4_MX_BLOCK) * np : size_t(G) * np * 2;
     const std::vector<double> what = smoothed_weight(W, N, K, lambda);
     std::vector<double> target = what, deq;
@@ -729,7 +749,8 @@ w4a4_status_t w4a4_codes_to_canonical(const uint8_t* q, int rows, int K, int fmt
       uint8_t* dst = out + size_t(r) * (K / 2) + size_t(g) * 32;
       if (fmt == W4A4_FMT_INT4_G64) {
         int v[W4A4_GROUP];
-        unfold_int4_group(src, v);
+        const uint8_t* x = q + int4_extra_offset(rp, K);
+        get_int4_group(src, x + (size_t(2 * g) * rp + r) * 8, x + (size_t(2 * g + 1) * rp + r) * 8, v);
         for (int b = 0; b < 32; ++b) dst[b] = uint8_t((v[2 * b] & 0xF) | ((v[2 * b + 1] & 0xF) << 4));
       } else {
         std::memcpy(dst, src, 32);
