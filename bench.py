@@ -6,12 +6,18 @@ One step = the whole hot path on one batch already resident in HBM: the activati
 (smoothing, group quantization, down projection X̂·L1) followed by the fused 4-bit GEMM with the
 low-rank up projection. Prints ONE JSON line on stdout (diagnostics go to stderr):
 
-  value      effective TOPS = (2·M·N·K + 2·M·r·(K+N)) / time per step (whole job, one GPU)
+  value      effective TOPS = (2·M·N·K + 2·M·r·(K+N)) / time per step, the step's time being the
+             median over the `steps` timed steps of the step's HIP-event time with cold caches (a
+             1 GiB buffer is overwritten before every step, outside the events, so no input is in
+             the 256 MB MALL or the L2s); the warm (back-to-back) step is reported beside it
   roofline   the GEMM kernel: algorithmic ops per launch / its average launch time (HIP events on
-             the launch stream around each GEMM launch of `steps` further steps, right after the
-             timed region) against the MI355X dense int8/fp8 MFMA peak (5.0 POP/s) for INT4 and
-             W8A8, or the MXFP4 peak (10.1 PFLOP/s) for the FP4 variant; also against the peak
-             measured on this GPU by register-only MFMA chains (libw4a4_peak.so)
+             the launch stream around each GEMM launch of the timed steps) against the MI355X
+             dense int8/fp8 MFMA peak (5.0 POP/s) for INT4 and W8A8, or the MXFP4 peak
+             (10.1 PFLOP/s) for the FP4 variant; also against the peak measured on this GPU by
+             register-only MFMA chains (libw4a4_peak.so)
+  configs    the other workloads of the pages' kernel-level claims, same protocol: the FLUX MLP
+             pair (fc2's activation side fused into fc1's GEMM, and consumer-side), the QKV layer
+             with a merged rank-16 LoRA (rank 48), and the MXFP4 layer at three batch sizes
   cpu_baseline  the numpy oracle's forward pass on a bounded sample of rows of the same layer
 """
 from __future__ import annotations
@@ -61,30 +67,71 @@ def gemm_kernel_name(fmt, rank_pad, M, N):
     return f"gemm_mx_small_kernel<{nt}>" if small else f"gemm_w8a8_kernel<{nt}, true>"
 
 
-def time_layer(lay, x, y, M, steps, warmup):
-    """ms per step (quantize + GEMM) by wall clock over `steps` steps, and the GEMM's average
-    launch time by HIP events on the launch stream (a separate pass)."""
+def new_flush(dev):
+    """A 1 GiB buffer; overwriting it evicts everything from the 256 MB MALL and the L2s."""
+    import torch
+    return torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+
+def cold_run(parts, n, flush):
+    """`n` steps of the callables `parts` (run in order on the current stream). Before each step the
+    flush buffer is overwritten (not timed); HIP events on the stream time every part. Returns the
+    per-step, per-part times [n, len(parts)] in ms and the wall-clock seconds of the whole loop
+    (flushes included)."""
     import torch
     stream = torch.cuda.current_stream()
-    acts = lay.act_buffers(M)
-    for _ in range(warmup):
-        lay.quantize(x)
-        lay.gemm(acts, M, y)
+    out = np.zeros((n, len(parts)))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        lay.quantize(x)
-        lay.gemm(acts, M, y)
+    for i in range(n):
+        flush.fill_(float(i & 7))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
+        ev[0].record(stream)
+        for k, f in enumerate(parts):
+            f()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        out[i] = [ev[k].elapsed_time(ev[k + 1]) for k in range(len(parts))]
+    return out, time.perf_counter() - t0
+
+
+def warm_run(parts, n):
+    """`n` back-to-back steps (no flush, no synchronization between them): wall-clock ms per step,
+    and per-part event times [n, len(parts)] from a second such pass."""
+    import torch
+    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for _ in range(n):
+        for f in parts:
+            f()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(n)]
     for e in evs:
-        lay.quantize(x)
         e[0].record(stream)
-        lay.gemm(acts, M, y)
-        e[1].record(stream)
+        for k, f in enumerate(parts):
+            f()
+            e[k + 1].record(stream)
     torch.cuda.synchronize()
-    return ms, float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    return ms, np.array([[e[k].elapsed_time(e[k + 1]) for k in range(len(parts))] for e in evs])
+
+
+def layer_parts(lay, x, y, M):
+    acts = lay.act_buffers(M)
+    return [lambda: lay.quantize(x), lambda: lay.gemm(acts, M, y)]
+
+
+def cold_summary(t, ops_step, gemm_col, gemm_ops, peak):
+    """Step and kernel figures of a cold run (t: [n, parts] ms)."""
+    step = t.sum(axis=1)
+    g = t[:, gemm_col]
+    return {"step_ms_cold": round(float(np.median(step)), 5),
+            "step_ms_cold_p10_p90": [pct(step, 10), pct(step, 90)],
+            "TOPS": round(ops_step / (np.median(step) * 1e-3) / 1e12, 2),
+            "kernels_ms_cold": [round(float(np.median(t[:, k])), 5) for k in range(t.shape[1])],
+            "gemm_ms_cold_mean": round(float(g.mean()), 5),
+            "roofline_frac": round(gemm_ops / (g.mean() * 1e-3) / 1e12 / peak, 4)}
 
 
 def traffic_from_profile(kernel_src: str):
@@ -195,95 +242,138 @@ def pct(v, q):
     return round(float(np.percentile(np.asarray(v), q)), 5)
 
 
-def mlp_bench(args):
-    """The FLUX MLP pair fc1 (4608 x 3072 -> 12288) -> GELU -> fc2 (12288 -> 3072), r 32, INT4. One
-    step = both layers. Fused: fc1's activation kernel, fc1's GEMM with fc2's activation side in its
-    epilogue (+ the t2 reduction), fc2's GEMM. Unfused: fc1's two kernels writing Y1, fc2's
-    activation kernel applying the GELU as it reads Y1, fc2's GEMM."""
+def mlp_setup(dev):
+    """The FLUX MLP pair fc1 (4608 x 3072 -> 12288) -> GELU -> fc2 (12288 -> 3072), r 32, INT4, and
+    the kernel lists of one step. Fused: fc1's activation kernel, fc1's GEMM with fc2's activation
+    side in its epilogue (+ the t2 reduction), fc2's GEMM. Consumer-side: fc1's two kernels writing
+    Y1, fc2's activation kernel applying the GELU as it reads Y1, fc2's GEMM."""
     import torch
     import synth
     import w4a4_quantized_gemm_smooth_amd as w4
-    dev = torch.device("cuda:0")
     d1, d2 = synth.workload("flux_mlp_fc1"), synth.workload("flux_mlp_fc2")
     M, K, N, N2, r = d1["M"], d1["K"], d1["N"], d2["N"], d1["rank"]
     log(f"[bench] flux_mlp: fc1 {M}x{K}->{N}, fc2 ->{N2}, r={r}")
     lam1, inv1 = w4.smooth_factors(w4.column_absmax(d1["x"]), w4.column_absmax(d1["w"]))
     lam2, inv2 = w4.smooth_factors(w4.column_absmax(d2["x"]), w4.column_absmax(d2["w"]))
-    fc1 = w4.W4A4Linear(w4.prepare_weights(d1["w"], lam1, r), inv1, device=dev)
-    fc2 = w4.W4A4Linear(w4.prepare_weights(d2["w"], lam2, r), inv2, device=dev)
-    pair = w4.MLPPair(fc1, fc2)
+    f1 = w4.W4A4Linear(w4.prepare_weights(d1["w"], lam1, r), inv1, device=dev)
+    f2 = w4.W4A4Linear(w4.prepare_weights(d2["w"], lam2, r), inv2, device=dev)
+    pair = w4.MLPPair(f1, f2)
     x = torch.from_numpy(np.ascontiguousarray(d1["x"]).view(np.int16)).to(dev).view(torch.bfloat16)
     y2 = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
-    ops = layer_ops(M, N, K, r) + layer_ops(M, N2, N, r)
-    stream = torch.cuda.current_stream()
     b = pair.buffers(M)
-    f1, f2, a2 = fc1, fc2, b["act2"]
+    a2 = b["act2"]
+    a1 = f1.act_buffers(M)
+    fused = [lambda: f1.quantize(x),
+             lambda: w4.lowrank_linear_gelu_quant(a1["xq"], a1["xscale"], a1["xl1"], f1.wq, f1.wscale, f1.l2t,
+                                                  f1.bias, M, N, K, r, f1.fmt, f2.inv_lambda, f2.l1t, f2.rank,
+                                                  a2["xq"], a2["xscale"], b["xl1_2_fused"]),
+             lambda: f2.gemm(dict(a2, xl1=b["xl1_2_fused"]), M, y2)]
+    unfused = [lambda: f1.quantize(x),
+               lambda: f1.gemm(a1, M, b["y1"]),
+               lambda: w4.gelu_quantize_act(b["y1"], f2.inv_lambda, f2.l1t, f2.rank, f2.fmt, a2["xq"], a2["xscale"],
+                                            a2["xl1"]),
+               lambda: f2.gemm(a2, M, y2)]
+    ops1, ops2 = layer_ops(M, N, K, r), layer_ops(M, N2, N, r)
+    return dict(M=M, K=K, N=N, N2=N2, r=r, fused=fused, unfused=unfused, ops1=ops1, ops2=ops2)
 
-    def fused_parts():
-        a1 = f1.quantize(x)
-        yield
-        w4.lowrank_linear_gelu_quant(a1["xq"], a1["xscale"], a1["xl1"], f1.wq, f1.wscale, f1.l2t, f1.bias, M, N, K, r,
-                                     f1.fmt, f2.inv_lambda, f2.l1t, f2.rank, a2["xq"], a2["xscale"], b["xl1_2_fused"])
-        yield
-        f2.gemm(dict(a2, xl1=b["xl1_2_fused"]), M, y2)
-        yield
 
-    def unfused_parts():
-        a1 = f1.quantize(x)
-        yield
-        f1.gemm(a1, M, b["y1"])
-        yield
-        w4.gelu_quantize_act(b["y1"], f2.inv_lambda, f2.l1t, f2.rank, f2.fmt, a2["xq"], a2["xscale"], a2["xl1"])
-        yield
-        f2.gemm(a2, M, y2)
-        yield
+def mlp_entries(mlp, n, warmup, flush):
+    """configs entries of the MLP pair: fused and consumer-side, cold, per kernel."""
+    out = {}
+    peak = PEAK_TOPS["int4_g64"]
+    ops = mlp["ops1"] + mlp["ops2"]
+    for name, parts, g1, g2 in (("flux_mlp_fused", mlp["fused"], 1, 2), ("flux_mlp_consumer_side", mlp["unfused"], 1, 3)):
+        for _ in range(warmup):
+            for f in parts:
+                f()
+        t, _ = cold_run(parts, n, flush)
+        e = cold_summary(t, ops, g1, mlp["ops1"], peak)
+        e["kernel"] = "gemm_kernel<0, 2, 2>" if g1 == 1 and name.endswith("fused") else "gemm_kernel<0, 2, -1>"
+        e["kernels"] = (["fc1_quantize_act", "fc1_gemm_with_fc2_activation_side", "fc2_gemm"] if g2 == 2 else
+                        ["fc1_quantize_act", "fc1_gemm", "fc2_gelu_quantize_act", "fc2_gemm"])
+        e["fc2_gemm_roofline_frac"] = round(mlp["ops2"] / (t[:, g2].mean() * 1e-3) / 1e12 / peak, 4)
+        e["ops_per_step"] = ops
+        out[name] = e
+    f, u = out["flux_mlp_fused"]["step_ms_cold"], out["flux_mlp_consumer_side"]["step_ms_cold"]
+    out["flux_mlp_fused"]["fusion_gain_pct"] = round(100.0 * (u - f) / u, 2)
+    return out
 
-    def run(parts, n):
-        for _ in range(n):
-            for _ in parts():
-                pass
 
-    def timed(parts):
-        run(parts, args.warmup)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        run(parts, args.steps)
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        per = []   # per-kernel event times, in a separate pass
-        for _ in range(args.steps):
-            evs = [torch.cuda.Event(enable_timing=True)]
-            evs[0].record(stream)
-            for _ in parts():
-                evs.append(torch.cuda.Event(enable_timing=True))
-                evs[-1].record(stream)
-            per.append(evs)
-        torch.cuda.synchronize()
-        kern = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in per])) for i in range(len(per[0]) - 1)]
-        return ms, kern
-
-    ms_f, k_f = timed(fused_parts)
-    ms_u, k_u = timed(unfused_parts)
-    fc1_ops = layer_ops(M, N, K, r)
+def mlp_bench(args):
+    """--workload flux_mlp: the fused MLP pair as the headline, with the consumer-side pair beside it."""
+    import torch
+    dev = torch.device("cuda:0")
+    mlp = mlp_setup(dev)
+    flush = new_flush(dev)
+    ent = mlp_entries(mlp, args.steps, args.warmup, flush)
+    f = ent["flux_mlp_fused"]
+    ops = f["ops_per_step"]
+    gemm_ms = f["gemm_ms_cold_mean"]
     out = {
         "metric": "effective TOPS of fused W4A4+rank-32 linear at FLUX shapes; % MFMA peak",
-        "value": round(ops / (ms_f * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_f, 5), "higher_is_better": True, "scaling": "weak",
+        "value": f["TOPS"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": f["step_ms_cold"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int4", "data": "synthetic (seeded FLUX-shaped MLP pair; random weights)",
-        "config": {"workload": "flux_mlp", "M": M, "K": K, "N": N, "N2": N2, "rank": r, "format": "int4_g64",
-                   "ops_per_step": ops, "path": "fc2's activation side fused into fc1's GEMM epilogue"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<0,2,2>", "achieved": round(fc1_ops / (k_f[1] * 1e-3) / 1e12, 2),
-                     "peak": PEAK_TOPS["int4_g64"], "unit": "TFLOP/s",
-                     "frac": round(fc1_ops / (k_f[1] * 1e-3) / 1e12 / PEAK_TOPS["int4_g64"], 4), "traffic": None,
-                     "avg_launch_ms": round(k_f[1], 5), "algorithmic_ops_per_launch": fc1_ops},
-        "kernels_fused_ms": {"fc1_quantize": round(k_f[0], 5), "fc1_gemm_gelu_quant_and_t2_reduce": round(k_f[1], 5),
-                             "fc2_gemm": round(k_f[2], 5)},
-        "kernels_unfused_ms": {"fc1_quantize": round(k_u[0], 5), "fc1_gemm": round(k_u[1], 5),
-                               "fc2_gelu_quantize": round(k_u[2], 5), "fc2_gemm": round(k_u[3], 5)},
-        "ablation": {"unfused_ms_per_step": round(ms_u, 5), "fused_ms_per_step": round(ms_f, 5),
-                     "fusion_gain_pct": round(100.0 * (ms_u - ms_f) / ms_u, 2)},
+        "config": {"workload": "flux_mlp", "M": mlp["M"], "K": mlp["K"], "N": mlp["N"], "N2": mlp["N2"],
+                   "rank": mlp["r"], "format": "int4_g64", "ops_per_step": ops, "caches": "cold",
+                   "path": "fc2's activation side fused into fc1's GEMM epilogue"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<0, 2, 2>",
+                     "achieved": round(mlp["ops1"] / (gemm_ms * 1e-3) / 1e12, 2), "peak": PEAK_TOPS["int4_g64"],
+                     "unit": "TOPS", "frac": f["roofline_frac"], "traffic": None, "avg_launch_ms": gemm_ms,
+                     "algorithmic_ops_per_launch": mlp["ops1"]},
+        "configs": ent,
     }
     print(json.dumps(out), flush=True)
+
+
+def lora_layer(dev):
+    """The FLUX QKV layer with a rank-16 LoRA merged into its low-rank branch (rank 32 + 16 = 48)."""
+    import synth
+    import w4a4_quantized_gemm_smooth_amd as w4
+    d = synth.workload("flux_qkv_lora")
+    lam, inv = w4.smooth_factors(w4.column_absmax(d["x"]), w4.column_absmax(d["w"]))
+    prep = w4.prepare_weights(d["w"], lam, 32, "int4_g64")
+    l1t, l2t, r2 = w4.append_lowrank(prep["l1t"], prep["l2t"], d["K"], d["N"], 32, d["lora_a"], d["lora_b"])
+    return d, w4.W4A4Linear(dict(prep, l1t=l1t, l2t=l2t, rank=r2, rank_pad=48), inv, device=dev)
+
+
+def configs_block(dev, n, warmup, flush):
+    """The configs entries beyond the headline layer (cold protocol, `n` steps each)."""
+    import torch
+    import synth
+    import w4a4_quantized_gemm_smooth_amd as w4
+    out = {}
+    t0 = time.perf_counter()
+    out.update(mlp_entries(mlp_setup(dev), n, warmup, flush))
+    log(f"[bench] configs: MLP pair done ({time.perf_counter() - t0:.0f}s)")
+    d, lay = lora_layer(dev)
+    M, K, N = d["M"], d["K"], d["N"]
+    x = torch.from_numpy(np.ascontiguousarray(d["x"]).view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    parts = layer_parts(lay, x, y, M)
+    warm_run(parts, warmup)
+    t, _ = cold_run(parts, n, flush)
+    ops = layer_ops(M, N, K, 48)
+    out["flux_qkv_lora_r48"] = dict(cold_summary(t, ops, 1, ops, PEAK_TOPS["int4_g64"]), kernel="gemm_kernel<0, 3, -1>",
+                                    kernels=["quantize_act", "gemm"], ops_per_step=ops)
+    del lay, x, y
+    d = synth.workload("mxfp4_sweep")
+    K, N, r = d["K"], d["N"], d["rank"]
+    lam, inv = w4.smooth_factors(w4.column_absmax(d["x"]), w4.column_absmax(d["w"]))
+    lay = w4.W4A4Linear(w4.prepare_weights(d["w"], lam, r, "mxfp4_b32"), inv, device=dev)
+    xall = torch.from_numpy(np.ascontiguousarray(d["x"]).view(np.int16)).to(dev).view(torch.bfloat16)
+    for M in d["batches"]:
+        x = xall[:M]
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        parts = layer_parts(lay, x, y, M)
+        warm_run(parts, warmup)
+        t, _ = cold_run(parts, n, flush)
+        ops = layer_ops(M, N, K, r)
+        out[f"mxfp4_m{M}"] = dict(cold_summary(t, ops, 1, ops, PEAK_TOPS["mxfp4_b32"]),
+                                 kernel=gemm_kernel_name("mxfp4_b32", 32, M, N), kernels=["quantize_act", "gemm"],
+                                 ops_per_step=ops)
+    log(f"[bench] configs done ({time.perf_counter() - t0:.0f}s)")
+    return out
 
 
 def cpu_baseline(d, lam, inv, budget_s=20.0):
@@ -334,6 +424,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the rank-0 (plain W4A4) comparison run")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (MLP pair, LoRA r48, MXFP4 sweep)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy a MIB-sized device buffer 3 times (a plain copy of known size, "
                          "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -366,61 +458,24 @@ def main():
     layer = w4.W4A4Linear(prep, inv, device=dev)
     x = torch.from_numpy(np.ascontiguousarray(d["x"]).view(np.int16)).to(dev).view(torch.bfloat16)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    acts = layer.act_buffers(M)
     stream = torch.cuda.current_stream()
 
-    def step():
-        layer.quantize(x)
-        layer.gemm(acts, M, y)
+    parts = layer_parts(layer, x, y, M)
+    warm_run(parts, args.warmup)
+    flush = new_flush(dev)
 
-    for _ in range(args.warmup):
-        step()
+    # the timed region: exactly `steps` steps, each preceded by a cache flush outside its events
     torch.cuda.synchronize()
-
-    # the timed region: exactly `steps` steps, nothing else on the stream
-    e_begin, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tc, wall = cold_run(parts, args.steps, flush)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e_begin.record(stream)
-    for i in range(args.steps):
-        step()
-    e_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms_step = e_begin.elapsed_time(e_end) / args.steps
-
-    # per-kernel launch durations: the same steps again, with HIP events on the launch stream
-    # between the kernels (outside the timed region: the events themselves cost a little time)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        evs[i][0].record(stream)
-        layer.quantize(x)
-        evs[i][1].record(stream)
-        layer.gemm(acts, M, y)
-        evs[i][2].record(stream)
-    torch.cuda.synchronize()
-    q_avg = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    g_avg = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-
-    # cold-cache view: overwrite a 1 GiB buffer (> 256 MB MALL + L2) before each step, kernels timed by events
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    cq, cg = [], []
-    for i in range(min(args.steps, 20)):
-        flush.fill_(float(i))
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        ev[0].record(stream)
-        layer.quantize(x)
-        ev[1].record(stream)
-        layer.gemm(acts, M, y)
-        ev[2].record(stream)
-        torch.cuda.synchronize()
-        cq.append(ev[0].elapsed_time(ev[1]))
-        cg.append(ev[1].elapsed_time(ev[2]))
-    del flush
+    step_c = tc.sum(axis=1)
+    ms_step = float(np.median(step_c))
+    q_c, g_c = tc[:, 0], tc[:, 1]
+    g_avg = float(g_c.mean())   # the GEMM's average launch time over the timed steps
+    # the warm view: back-to-back steps, inputs left in the MALL by the previous step
+    warm_ms, tw = warm_run(parts, args.steps)
 
     ops = layer_ops(M, N, K, r)
-    ms_step = wall * 1e3 / args.steps
     value = ops / (ms_step * 1e-3) / 1e12
     achieved = ops / (g_avg * 1e-3) / 1e12
     peak = PEAK_TOPS[fmt]
@@ -430,79 +485,79 @@ def main():
     qbytes = quantize_bytes(M, K, r, fmt)
     traffic = traffic_from_profile(os.path.join(ROOT, "w4a4_quantized_gemm_smooth_amd", "csrc", "w4a4_device.hip")) \
         if args.workload == "flux_qkv" and fmt == "int4_g64" else None
+    q_med = float(np.median(q_c))
     out = {
         "metric": "effective TOPS of fused W4A4+rank-32 linear at FLUX shapes; % MFMA peak",
         "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "event_ms_per_step": round(ev_ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": DTYPE[fmt], "data": "synthetic (seeded FLUX-shaped layer; random weights)",
         "config": {"workload": args.workload, "M": M, "K": K, "N": N, "rank": r, "format": fmt,
-                   "ops_per_step": ops, "peak_frac_of_step": round(value / peak, 4)},
+                   "ops_per_step": ops, "caches": "cold (1 GiB overwritten before each step, not timed)",
+                   "peak_frac_of_step": round(value / peak, 4)},
+        "timing": {"ms_per_step_cold_median": round(ms_step, 5),
+                   "ms_per_step_cold_p10_p90": [pct(step_c, 10), pct(step_c, 90)],
+                   "ms_per_step_warm": round(warm_ms, 5),
+                   "TOPS_warm": round(ops / (warm_ms * 1e-3) / 1e12, 2),
+                   "wall_s_timed_loop_incl_flushes": round(wall, 4)},
         "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(fmt, prep["rank_pad"], M, prep["N"]),
-                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "avg_launch_ms": round(g_avg, 5), "algorithmic_ops_per_launch": ops,
                      "peak_measured": peak_meas,
                      "frac_measured": None if not peak_meas else round(achieved / peak_meas, 4),
                      "measured_mfma_peaks_TOPS": peaks},
         "kernels": {
-            "quantize_act": {"avg_ms_warm": round(q_avg, 5), "avg_ms_cold": round(float(np.mean(cq)), 5),
-                             "cold_median_p10_p90_ms": [pct(cq, 50), pct(cq, 10), pct(cq, 90)],
+            "quantize_act": {"ms_cold_median_p10_p90": [round(q_med, 5), pct(q_c, 10), pct(q_c, 90)],
+                             "ms_warm_mean": round(float(tw[:, 0].mean()), 5),
                              "algorithmic_bytes": qbytes,
-                             "GB/s_cold": round(qbytes / (np.median(cq) * 1e-3) / 1e9, 1),
-                             "hbm_frac_cold": round(qbytes / (np.median(cq) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "GB/s_cold": round(qbytes / (q_med * 1e-3) / 1e9, 1),
+                             "hbm_frac_cold": round(qbytes / (q_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                              "copy_GB/s_measured": round(copy_gbs, 1),
-                             "frac_of_copy_cold": round(qbytes / (np.median(cq) * 1e-3) / 1e9 / copy_gbs, 4)},
-            "gemm": {"avg_ms_warm": round(g_avg, 5), "avg_ms_cold": round(float(np.mean(cg)), 5),
-                     "cold_median_p10_p90_ms": [pct(cg, 50), pct(cg, 10), pct(cg, 90)],
-                     "TOPS_cold": round(ops / (np.median(cg) * 1e-3) / 1e12, 2)},
+                             "frac_of_copy_cold": round(qbytes / (q_med * 1e-3) / 1e9 / copy_gbs, 4)},
+            "gemm": {"ms_cold_median_p10_p90": [pct(g_c, 50), pct(g_c, 10), pct(g_c, 90)],
+                     "ms_cold_mean": round(g_avg, 5), "ms_warm_mean": round(float(tw[:, 1].mean()), 5),
+                     "TOPS_cold": round(ops / (np.median(g_c) * 1e-3) / 1e12, 2)},
         },
     }
     if not args.no_ablation and r > 0:
         # the same layer without the low-rank branch (rank 0: plain W4A4 on the smoothed weight),
         # to report the branch's overhead (§4.3: fused, it should add only a few percent)
+        n_ab = min(args.steps, 20)
         prep0 = w4.prepare_weights(d["w"], lam, 0, fmt)
         layer0 = w4.W4A4Linear(prep0, inv, device=dev)
-        acts0 = layer0.act_buffers(M)
-        for _ in range(args.warmup):
-            layer0.quantize(x)
-            layer0.gemm(acts0, M, y)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            layer0.quantize(x)
-            layer0.gemm(acts0, M, y)
-        torch.cuda.synchronize()
-        ms0 = (time.perf_counter() - t0) * 1e3 / args.steps
+        p0 = layer_parts(layer0, x, y, M)
+        warm_run(p0, args.warmup)
+        ms0 = float(np.median(cold_run(p0, n_ab, flush)[0].sum(axis=1)))
         # the same branch unfused: separate library GEMMs that re-read X and Y (the pages' baseline)
         l1s, l2 = unfused_lowrank_factors(prep, inv, dev)
         layer_u = unfused_layer(prep, inv, dev)
         acts_u = layer_u.act_buffers(M)
-        for _ in range(args.warmup):
-            unfused_step(layer_u, acts_u, x, y, l1s, l2)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            unfused_step(layer_u, acts_u, x, y, l1s, l2)
-        torch.cuda.synchronize()
-        msu = (time.perf_counter() - t0) * 1e3 / args.steps
-        out["ablation"] = {"rank0_ms_per_step": round(ms0, 5),
+        pu = [lambda: unfused_step(layer_u, acts_u, x, y, l1s, l2)]
+        warm_run(pu, args.warmup)
+        msu = float(np.median(cold_run(pu, n_ab, flush)[0].sum(axis=1)))
+        out["ablation"] = {"caches": "cold", "rank0_ms_per_step": round(ms0, 5),
                            "lowrank_overhead_pct": round(100.0 * (ms_step - ms0) / ms0, 2),
                            "unfused_ms_per_step": round(msu, 5),
                            "unfused_lowrank_overhead_pct": round(100.0 * (msu - ms0) / ms0, 2)}
-        del layer0, acts0, layer_u, acts_u, l1s, l2
+        del layer0, layer_u, acts_u, l1s, l2
         if fmt != "w8a8":
             # the 8-bit setting of App. D (per-token / per-channel INT8, rank 16) on the same layer:
             # its rank-16 factors are the leading 16 of this layer's SVD factors
             r8 = min(16, r)
             prep8 = w4.prepare_weights(d["w"], lam, r8, "w8a8", prep["l1"][:, :r8], prep["l2"][:r8])
             layer8 = w4.W4A4Linear(prep8, inv, device=dev)
-            ms8, g8 = time_layer(layer8, x, y, M, args.steps, args.warmup)
+            p8 = layer_parts(layer8, x, y, M)
+            warm_run(p8, args.warmup)
+            t8 = cold_run(p8, n_ab, flush)[0]
+            ms8 = float(np.median(t8.sum(axis=1)))
             ops8 = layer_ops(M, N, K, r8)
             out["ablation"].update({"w8a8_rank": r8, "w8a8_ms_per_step": round(ms8, 5),
-                                    "w8a8_gemm_avg_ms": round(g8, 5),
-                                    "w8a8_gemm_TOPS": round(ops8 / (g8 * 1e-3) / 1e12, 2),
+                                    "w8a8_gemm_ms": round(float(t8[:, 1].mean()), 5),
+                                    "w8a8_gemm_TOPS": round(ops8 / (t8[:, 1].mean() * 1e-3) / 1e12, 2),
                                     "speedup_vs_w8a8": round(ms8 / ms_step, 3)})
             del layer8, prep8
+    if not args.no_configs and args.workload == "flux_qkv" and not args.format and not args.batch:
+        out["configs"] = configs_block(dev, min(args.steps, 20), min(args.warmup, 5), flush)
     if args.copy_calibration:
         n = args.copy_calibration << 18   # float32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)

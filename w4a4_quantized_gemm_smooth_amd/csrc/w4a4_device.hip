@@ -41,19 +41,13 @@ namespace {
 // 6f). Half h (runs 2h, 2h+1) is one lane's 6-dword MFMA operand, split into a 16-byte main part
 // [d0 d1 d2 of run 2h, d0 of run 2h+1] at byte (g·rows_pad + row)·32 + 16h and an 8-byte extra part
 // [d1 d2 of run 2h+1] at byte rows_pad·K/2 + ((2g + h)·rows_pad + row)·8 of the code buffer.
-// Byte offsets of run kc's three image dwords (kc = 0..3), for a row of group g:
-__device__ __forceinline__ void int4_run_offsets(int g, int row, int rows_pad, int K, int kc, int (&off)[3]) {
-  const int h = kc >> 1, main = (g * rows_pad + row) * 32 + 16 * h;
-  if ((kc & 1) == 0) {
-    off[0] = main;
-    off[1] = main + 4;
-    off[2] = main + 8;
-  } else {
-    const int extra = rows_pad * (K / 2) + ((2 * g + h) * rows_pad + row) * 8;
-    off[0] = main + 12;
-    off[1] = extra;
-    off[2] = extra + 4;
-  }
+// Byte offset of the part that run kc (kc = 0..3) of a row of group g stores whole: run 2h the 16-byte
+// main part of half h (its own three dwords and run 2h+1's first, taken from that run's lane), run
+// 2h+1 the 8-byte extra part (its other two dwords).
+__device__ __forceinline__ int int4_part_offset(int g, int row, int rows_pad, int K, int kc) {
+  const int h = kc >> 1;
+  return (kc & 1) == 0 ? (g * rows_pad + row) * 32 + 16 * h
+                       : rows_pad * (K / 2) + ((2 * g + h) * rows_pad + row) * 8;
 }
 
 // GELU(y) = (y/2)·(1 + erf(y/√2)) in fp32, erf from Abramowitz & Stegun 7.1.28
@@ -319,15 +313,17 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
         od[8 + e] = xb[2 * e + 1] * ib;
       }
       const v6i img = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
-      // the image dwords of this lane's run of each group go straight to the code layout
-      int oa[3], ob[3];
-      int4_run_offsets(ga, row, m_pad, K, kc, oa);
-      int4_run_offsets(gb, row, m_pad, K, kc, ob);
-#pragma unroll
-      for (int d = 0; d < 3; ++d) {
-        __builtin_amdgcn_raw_buffer_store_b32(img[d], qr, oa[d], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(img[3 + d], qr, two ? ob[d] : OOB, 0, 0);
-      }
+      // the even-kc lane of each pair (lanes r + 16 kc, r + 16 (kc + 1)) stores the main part, the
+      // odd one the extra part: one lane swap brings the odd run's first dword to its partner
+      // (the swap's second result holds, in the even rows of 16 lanes, the odd rows' values)
+      const bool main_lane = (kc & 1) == 0;
+      const auto pa = __builtin_amdgcn_permlane16_swap(img[0], img[0], false, false);
+      const auto pb = __builtin_amdgcn_permlane16_swap(img[3], img[3], false, false);
+      const int oa = int4_part_offset(ga, row, m_pad, K, kc), ob = two ? int4_part_offset(gb, row, m_pad, K, kc) : OOB;
+      __builtin_amdgcn_raw_buffer_store_b128(v4i{img[0], img[1], img[2], (int)pa[1]}, qr, main_lane ? oa : OOB, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(v2i{img[1], img[2]}, qr, main_lane ? OOB : oa, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v4i{img[3], img[4], img[5], (int)pb[1]}, qr, main_lane ? ob : OOB, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(v2i{img[4], img[5]}, qr, main_lane ? OOB : ob, 0, 0);
       // the four lanes of a row store the same scale
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne(sa), sr, (ga * m_pad + row) * 2, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne(sb), sr, two ? (gb * m_pad + row) * 2 : OOB, 0, 0);
@@ -919,12 +915,15 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
       }
       uint32_t sb;
       const uint3 q = quant_int4_lane(xh, sb);
-      if (gvalid) {
-        int off[3];
-        int4_run_offsets(g2, row, m_pad, N, kc, off);
-        reinterpret_cast<uint32_t*>(fa.xq2 + off[0])[0] = q.x;
-        reinterpret_cast<uint32_t*>(fa.xq2 + off[1])[0] = q.y;
-        reinterpret_cast<uint32_t*>(fa.xq2 + off[2])[0] = q.z;
+      if (gvalid) {  // wave-uniform: every lane takes part in the lane swap
+        // even-kc lanes store the 16-byte main part (with the odd partner's first dword), odd-kc
+        // lanes the 8-byte extra part
+        const auto pq = __builtin_amdgcn_permlane16_swap(q.x, q.x, false, false);
+        uint8_t* const dst = fa.xq2 + int4_part_offset(g2, row, m_pad, N, kc);
+        if ((kc & 1) == 0)
+          *reinterpret_cast<uint4*>(dst) = make_uint4(q.x, q.y, q.z, pq[1]);
+        else
+          *reinterpret_cast<uint2*>(dst) = make_uint2(q.y, q.z);
         if (kc == 0) fa.xs2[(size_t)g2 * m_pad + row] = (uint16_t)sb;
       }
       if constexpr (NT2 > 0) {
