@@ -27,6 +27,7 @@
 //  * The low-rank branch uses the bf16 MFMAs (16x16x32 for the down projection, 32x32x16 for the
 //    up projection, accumulating straight into the GEMM accumulators).
 
+#include <atomic>
 #include <mutex>
 
 #include "w4a4_device_common.h"
@@ -73,6 +74,16 @@ __device__ __forceinline__ float gelu32(float y) {
   e = u < 0.f ? -e : e;
   return (0.5f * y) * (1.0f + e);
 }
+
+// The GELU of a bf16 input rounded to bf16 takes one of 65536 values: this table holds
+// bf16(gelu32(x)) for every bf16 bit pattern x, filled once per device by gelu_table_kernel with
+// the function above, so a lookup returns exactly what evaluating gelu32 would.
+static __device__ uint16_t gelu_tab[65536];
+__global__ void gelu_table_kernel() {
+  const uint32_t x = blockIdx.x * 256 + threadIdx.x;
+  gelu_tab[x] = (uint16_t)bf16_rne(gelu32(bf16f(x)));
+}
+__device__ __forceinline__ uint32_t gelu_bf16(uint32_t bits) { return gelu_tab[bits & 0xFFFFu]; }
 
 // INT4 codes of one group row held by four lanes (lane bits 4-5 = kc, 16 values each): s =
 // bf16(max|X̂| / 7) (0 below 2^-126), q = rint(X̂ · (1/s)) (|q| <= 7 by the symmetric scale). The fp32
@@ -173,13 +184,15 @@ __device__ __forceinline__ void scale_pair(const float (&ua)[16], const float (&
 
 template <bool GELU_IN>
 __device__ __forceinline__ void unpack16(const v4i (&xv)[2], float (&u)[16]) {
+  uint32_t bits[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const uint32_t w = (uint32_t)xv[e >> 3][(e >> 1) & 3];
-    uint32_t bits = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-    if (GELU_IN) bits = bf16_rne(gelu32(bf16f(bits)));
-    u[e] = bf16f(bits);
+    bits[e] = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+    if (GELU_IN) bits[e] = gelu_bf16(bits[e]);  // the 16 table reads go out together
   }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) u[e] = bf16f(bits[e]);
 }
 
 // X̂ = fp32(x · (1/λ)), one fp32 multiply per value (no contraction: nothing to fuse)
@@ -885,6 +898,19 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
   }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    // the half's 64 GELU values per lane: every table read issued before the first is used (the
+    // reads are unconditional; rows past M are zeroed afterwards)
+    uint32_t gx[2][2][16];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const uint32_t y = pack_bf16x2(acc[2 * half + ii][j][v] + bcol[j], acc[2 * half + ii][j][v + 1] + bcol[j]);
+          gx[ii][j][v] = gelu_bf16(y);
+          gx[ii][j][v + 1] = gelu_bf16(y >> 16);
+        }
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -893,12 +919,9 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
         for (int v = 0; v < 16; v += 2) {
           const int rl = ii * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
           const int grow = m0 + wm * 128 + half * 64 + rl;  // rows grow, grow + 1
-          const uint32_t y = pack_bf16x2(acc[2 * half + ii][j][v] + bcol[j], acc[2 * half + ii][j][v + 1] + bcol[j]);
-          const uint32_t x0 = grow < M ? bf16_rne(gelu32(bf16f(y & 0xFFFFu))) : 0u;
-          const uint32_t x1 = grow + 1 < M ? bf16_rne(gelu32(bf16f(y >> 16))) : 0u;
           uint16_t* d = reinterpret_cast<uint16_t*>(stage + rl * Y_ES + (j * 32 + lr) * 2);
-          d[0] = (uint16_t)x0;
-          d[Y_ES / 2] = (uint16_t)x1;
+          d[0] = (uint16_t)(grow < M ? gx[ii][j][v] : 0u);
+          d[Y_ES / 2] = (uint16_t)(grow + 1 < M ? gx[ii][j][v + 1] : 0u);
         }
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
@@ -1162,6 +1185,31 @@ __global__ __launch_bounds__(MX_THREADS, 2) void gemm_mx_small_kernel(
 }
 
 // ----------------------------------------------------------------------------- launch helpers
+// The GELU table of the current device, filled on first use: on `st`, then waited for, so that calls
+// on any stream find it complete. A failed fill (e.g. a first call during stream capture, where
+// waiting is not allowed) is retried by the next call.
+hipError_t ensure_gelu_table(hipStream_t st) {
+  constexpr int MAXD = 64;
+  static std::atomic<bool> ready[MAXD];
+  static std::mutex mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAXD) return hipErrorInvalidDevice;
+  if (ready[dev].load(std::memory_order_acquire)) return hipSuccess;
+  try {
+    std::lock_guard<std::mutex> lock(mu);
+    if (ready[dev].load(std::memory_order_relaxed)) return hipSuccess;
+    hipLaunchKernelGGL(gelu_table_kernel, dim3(65536 / 256), dim3(256), 0, st);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e == hipSuccess) ready[dev].store(true, std::memory_order_release);
+    return e;
+  } catch (...) {  // std::mutex::lock reports failure by throwing
+    return hipErrorUnknown;
+  }
+}
+
 template <int FMT, int NT, bool GELU_IN = false>
 hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, const uint16_t* l1t, int m_pad,
                      uint8_t* xq, void* xs, float* xl1, hipStream_t st) {
@@ -1317,6 +1365,7 @@ w4a4_status_t w4a4_gelu_quantize_act(const uint16_t* Y, int M, int K, int ldy, c
   if (ldy < K || ldy % 8 != 0 || ldy > QA_MAX_LDX) return W4A4_ERR_INVALID_ARG;
   if (!aligned16(Y) || !aligned16(inv_lambda) || !aligned16(xq) || !aligned16(xscale)) return W4A4_ERR_INVALID_ARG;
   if (rank > 0 && (!l1t || !xl1 || !aligned16(l1t) || !aligned16(xl1))) return W4A4_ERR_INVALID_ARG;
+  if (ensure_gelu_table(reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return W4A4_ERR_HIP;
   const hipError_t e = dispatch_qa<W4A4_FMT_INT4_G64, true>(rank_pad_of(rank) / 16, Y, M, K, ldy, inv_lambda, l1t,
                                                             rows_pad_of(M), xq, xscale, xl1,
                                                             reinterpret_cast<hipStream_t>(stream));
@@ -1398,6 +1447,7 @@ w4a4_status_t w4a4_lowrank_linear_gelu_quant(const uint8_t* xq, const void* xsca
   const int tiles_n = n_pad / 256;
   GeluQuantArgs fa{inv_lambda2, l1t2, xq2, static_cast<uint16_t*>(xscale2),
                    rank2 > 0 ? (tiles_n > 1 ? xl1_2 + (size_t)m_pad * rp2 : xl1_2) : nullptr};
+  if (ensure_gelu_table(reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return W4A4_ERR_HIP;
   const hipError_t e = dispatch_gemm_gelu_quant(rank_pad_of(rank) / 16, rp2 / 16, xq, xscale, xl1, wq, wscale, l2t,
                                                 bias, Y, ldy, M, N, K, m_pad, n_pad, fa, xl1_2,
                                                 reinterpret_cast<hipStream_t>(stream));
@@ -1421,6 +1471,7 @@ w4a4_status_t w4a4_lowrank_linear_gelu_quant_noalloc(const uint8_t* xq, const vo
   if (planes && scratch_of_current_device(&part) != hipSuccess) return W4A4_ERR_HIP;
   GeluQuantArgs fa{inv_lambda2, l1t2, xq2, static_cast<uint16_t*>(xscale2),
                    rank2 > 0 ? (planes ? part : t2) : nullptr};
+  if (ensure_gelu_table(reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return W4A4_ERR_HIP;
   const hipError_t e = dispatch_gemm_gelu_quant(rank_pad_of(rank) / 16, rp2 / 16, xq, xscale, xl1, wq, wscale, l2t,
                                                 bias, Y, ldy, M, N, K, m_pad, n_pad, fa, t2,
                                                 reinterpret_cast<hipStream_t>(stream));
