@@ -87,15 +87,15 @@ const char* w4a4_status_str(w4a4_status_t status);
  * Buffer sizes and layouts. K must be a positive multiple of 64 for every format (the MXFP4
  * kernels step K by two 32-blocks). m_pad = roundup(M, 256), n_pad = roundup(N, 256),
  * rank_pad = roundup(rank, 16) (0 for rank 0). Layouts (G64 = K/64, B32 = K/32):
- *   wq     [G64][n_pad][32] bytes : the 64 codes of (row, group), 4 bits each.
- *            MXFP4: code k of the group at byte k/2, low nibble for even k (E2M1 codes).
- *            INT4 (folded FP6 image): the 8 little-endian dwords d0..d7 hold codes 16j..16j+15
- *            in the pair (d[2j], d[2j+1]). With F_f = (q < 0) << 5 | |q| for code 16j + f (the
- *            FP6 E2M3 encoding of q/8) and the 96-bit image I = Σ_f F_f << 6f split into dwords
- *            o0, o1, o2: d[2j] = (o0 & 0xE79E79E7) | (o1 & 0x18618618),
- *            d[2j+1] = (o1 & 0x61861861) | (o2 & 0x9E79E79E). (Bits 3-4 of every 6-bit field
- *            are zero, which leaves room for o1 in o0 and o2.) The GEMM unfolds this into FP6
- *            MFMA operands with four AND / AND-OR operations per 16 codes.
+ *   wq     MXFP4: [G64][n_pad][32] bytes, the 64 codes of (row, group) 4 bits each: code k of the
+ *            group at byte k/2, low nibble for even k (E2M1 codes).
+ *          INT4 (FP6 images, n_pad·K·3/4 bytes): code q is carried as the FP6 E2M3 field
+ *            F = (q < 0) << 5 | |q| (the encoding of q/8). The 64 codes of (row, group g) form four
+ *            runs of 16; run j's fields F_f (f = 0..15, code 16j + f) make the 96-bit image
+ *            Σ_f F_f << 6f, dwords o0 o1 o2 (little-endian). Half h (runs 2h, 2h+1) is stored as a
+ *            16-byte main part [o0 o1 o2 of run 2h, o0 of run 2h+1] at byte (g·n_pad + row)·32 + 16h
+ *            and an 8-byte extra part [o1 o2 of run 2h+1] at byte n_pad·K/2 + ((2g + h)·n_pad + row)·8.
+ *            The GEMM feeds these images to its FP6 MFMAs as they are.
  *   wscale INT4: [G64][n_pad] bf16;  MXFP4: [B32][n_pad] E8M0 bytes (e + 127)
  *   W8A8:  wq [B32][n_pad][32] int8 codes (code k of the 32-slice at byte k);
  *          wscale [n_pad] fp32 (one scale per output channel)
@@ -107,6 +107,7 @@ const char* w4a4_status_str(w4a4_status_t status);
  *   xl1    fp32, first [m_pad][rank_pad] : t = bf16(X̂)·L1 (fp32 accumulation); the rest of the
  *          buffer (when the size returned here exceeds m_pad·rank_pad·4 bytes) is scratch that
  *          w4a4_quantize_act uses for per-K-slice partial sums of t. 0 bytes when rank == 0.
+ *          w4a4_lowrank_linear reads only the first m_pad·rank_pad floats.
  * Returns W4A4_ERR_INVALID_ARG for M, N < 1, K not a positive multiple of 64, rank outside
  * [0, min(N, K, W4A4_MAX_RANK)], or out == NULL; W4A4_ERR_UNSUPPORTED for an unknown fmt.
  */
@@ -203,7 +204,7 @@ w4a4_status_t w4a4_scales_to_canonical(const void* s, int rows, int K, int fmt, 
  *   (INT4: s = bf16(max|X̂|/7), q = rint(X̂ · (1/s)); MXFP4: e = min{e : 6·2^e >= max|X̂|},
  *   E2M1 round-half-even of X̂ / 2^e; W8A8, per row over all of K: s = fp32(max|X̂|/127),
  *   q = clamp(rint(X̂ · (1/s)), -127, 127)); t = bf16(X̂) · L1 accumulated in fp32.
- *   X          [M][ldx] bf16 device, ldx >= K, ldx % 8 == 0
+ *   X          [M][ldx] bf16 device, K <= ldx <= 2^26, ldx % 8 == 0 (W4A4_ERR_INVALID_ARG otherwise)
  *   inv_lambda [K] fp32 device
  *   l1t        [rank_pad][K] bf16 device (NULL allowed when rank == 0)
  *   xq, xscale, xl1 device outputs in library layout (xl1 may be NULL when rank == 0).
@@ -237,10 +238,14 @@ w4a4_status_t w4a4_lowrank_linear(const uint8_t* xq, const void* xscale, const f
  * names no formula): GELU(y) = (y/2)(1 + erf(y/sqrt 2)) in fp32 with erf from Abramowitz & Stegun
  * 7.1.28, 1 - (1 + a1 x + ... + a6 x^6)^-16, |error| <= 3e-7, evaluated one IEEE fp32 operation at a
  * time (Horner from a6, the 16th power by four squarings, correctly rounded division), so that
- * the bf16 rounding of X2 = bf16(GELU(Y1)) is reproducible on a host.
+ * the bf16 rounding of X2 = bf16(GELU(Y1)) is reproducible on a host. The first GELU call on a
+ * device evaluates it once for every bf16 input into a table in the library's device data (on the
+ * call's stream, waiting for it; not possible during stream capture, where it returns
+ * W4A4_ERR_HIP and is retried by the next call); later calls look the values up.
  *
  * Consumer side: w4a4_quantize_act (INT4 only) applied to X = bf16(GELU(Y)) of a producer's bf16
- * output Y [M][ldy] (device); every other argument as for w4a4_quantize_act.
+ * output Y [M][ldy] (device; K <= ldy <= 2^26, ldy % 8 == 0); every other argument as for
+ * w4a4_quantize_act.
  */
 w4a4_status_t w4a4_gelu_quantize_act(const uint16_t* Y, int M, int K, int ldy, const float* inv_lambda,
                                      const uint16_t* l1t, int rank, int fmt,

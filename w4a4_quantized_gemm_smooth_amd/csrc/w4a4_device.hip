@@ -16,9 +16,9 @@
 //    (E2M3) operands, which issues at twice the fp8 rate. A code q (|q| <= 7) is carried as the
 //    E2M3 subnormal sign|00|mag, whose value is q / 8, so every product and every partial sum of
 //    one 64-wide group is exact in fp32 (the result is Σ q_x q_w / 64, |Σ| <= 3136). One
-//    32x32x64 MFMA is exactly one group. The codes stay 4 bits wide in memory: each 16-code run
-//    is stored as its 96-bit FP6 image folded into 64 bits (the zero exponent bits of the outer
-//    dwords hold the middle dword), and four AND/AND-OR ops per 16 codes unfold it for the MFMA.
+//    32x32x64 MFMA is exactly one group. The codes are stored as these FP6 images (6 bits per
+//    code: a 16-byte main part and an 8-byte extra part per half row-group), so the GEMM reads its
+//    MFMA operands from LDS as they are.
 //  * The per-group scale product s_x[m,g] * s_w[n,g] of a 32x32 tile is produced as an exact
 //    outer product by one bf16 MFMA (v_mfma_f32_32x32x8_bf16 with one non-zero k), so the
 //    group epilogue costs one fp32 FMA per output element.
