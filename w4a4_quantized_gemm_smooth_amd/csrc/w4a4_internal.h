@@ -41,8 +41,9 @@ inline w4a4_status_t check_shape(int M, int N, int K, int rank, int fmt) {
 // Activation kernel blocking: 64 rows x a slice of at most QA_MAX_GS groups per block, so the
 // slice's L1 rows are fetched once per 64 rows. With several slices each block writes the partial t
 // of its slice to a scratch plane behind t, and a second kernel sums the planes in slice order
-// (deterministic). Cross-block reduction inside one kernel would need device-scope release fences,
-// which write back the per-XCD L2s.
+// (deterministic). A reduction inside the kernel (the last block of a row block to finish sums the
+// planes) needs every block to wait for its partial to be written through to the device-coherent
+// level before it counts itself, which costs more than the second launch.
 #ifndef W4A4_QA_BLOCK_ROWS  // build-time tuning knobs (rows per block: a multiple of 16, at most 256)
 #define W4A4_QA_BLOCK_ROWS 64
 #endif
