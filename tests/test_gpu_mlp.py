@@ -142,6 +142,43 @@ def test_producer_side_fusion_without_y1():
     assert torch.equal(a2b["xq"], codes) and torch.equal(a2b["xscale"], scales) and torch.equal(a2b["xl1"], t)
 
 
+def test_gelu_of_every_finite_bf16_input():
+    """The device GELU on every finite bf16 pattern (65280 of them, as a 510 x 128 fc1 output) through
+    fc2's activation kernel with 1/λ₂ = 1 and L1₂ the 128 x 128 identity (rank 128): then
+    t₂ = bf16(X̂₂)·L1₂ is X₂ = bf16(GELU(Y₁)) itself, one exact product per entry, so every GELU value
+    is compared with the oracle's. A subnormal X₂ may come back as 0 (bf16 MFMA inputs) and -0 as +0
+    (a sum with signed zeros); every other entry must match exactly. Codes and scales of the same X₂
+    bit-exact."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    y1_bits = bits[((bits >> 7) & 0xFF) != 0xFF].reshape(510, 128)
+    m, k, r = 510, 128, 128
+    print(f"[gelu every bf16] M={m} K={k} r={r}", flush=True)
+    inv2 = np.ones(k, np.float32)
+    l1 = np.eye(k, r, dtype=np.float32)
+    act = O.gelu_quantize(y1_bits, inv2, l1)
+    x2 = O.bf16_bits_to_f32(act["x2_bits"])
+    assert np.array_equal(act["t"], x2.astype(np.float64)), "oracle: t must be X2 for an identity L1"
+    sz = w4.buffer_sizes(m, r, k, r)
+    y1 = torch.from_numpy(np.ascontiguousarray(y1_bits).view(np.int16)).cuda().view(torch.bfloat16)
+    l1t = torch.from_numpy(O.f32_to_bf16_bits(np.ascontiguousarray(l1.T)).view(np.int16)).cuda()
+    xq = torch.empty(sz["xq"], dtype=torch.uint8, device="cuda")
+    xs = torch.empty(sz["xscale"], dtype=torch.uint8, device="cuda")
+    xl1 = torch.empty(sz["xl1"] // 4, dtype=torch.float32, device="cuda")
+    w4.gelu_quantize_act(y1, torch.ones(k, dtype=torch.float32, device="cuda"), l1t, r, "int4_g64", xq, xs, xl1)
+    torch.cuda.synchronize()
+    codes = w4.codes_to_canonical(xq.cpu().numpy(), m, k, "int4_g64")
+    scales = w4.scales_to_canonical(xs.cpu().numpy(), m, k, "int4_g64")
+    assert np.array_equal(codes, O.pack_int4(act["cx"])), "codes differ"
+    assert np.array_equal(scales, O.f32_to_bf16_bits(act["sx"])), "scales differ"
+    mp = sz["m_pad"]
+    t = xl1.cpu().numpy()[: mp * r].reshape(mp, r)[:m]
+    normal = np.abs(x2) >= 2.0 ** -126
+    bad = normal & (t != x2)
+    assert not bad.any(), f"{bad.sum()} GELU values differ, e.g. input {hex(int(y1_bits[bad][0]))}"
+    sub = ~normal
+    assert np.all((t[sub] == x2[sub]) | (t[sub] == 0)), "a subnormal GELU value came back neither exact nor 0"
+
+
 def test_full_size_flux_mlp_fused():
     """FLUX MLP: fc1 4608 x 3072 -> 12288 with fc2's activation side (K 12288, r 32) in its
     epilogue: all fc2 codes and scales bit-exact against the oracle from the GPU's Y1, t2 on

@@ -235,6 +235,54 @@ def test_deterministic_and_stream():
 
 
 @pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
+def test_graph_capture_and_replay(fmt):
+    """The layer step (activation side, then the GEMM) captured once in a HIP graph: the library's
+    launches allocate nothing and clear nothing, so the graph replays it. Three replays, each on new
+    activations copied into the captured input and with eager library calls on other buffers in
+    between; every replay bit-exact against the eager step on the same input, and the first against
+    the oracle."""
+    m, k, n, r = 700, 384, 520, 24
+    d = synth.make_layer(m, k, n, n_outliers=4, outlier_scale=30.0, seed=21)
+    lam, inv = _smooth(d)
+    ref = oracle_weights(d, r, fmt, lam)
+    bf = lambda a: O.f32_to_bf16_bits(a)
+    lay = w4.W4A4Linear(w4.prepare_weights(d["w"], lam, r, fmt, bf(ref["l1"]), bf(ref["l2"])), inv)
+    print(f"[graph replay] fmt={fmt} M={m} K={k} N={n} r={r}", flush=True)
+    xs = [synth.make_layer(m, k, n, n_outliers=4, outlier_scale=30.0, seed=21 + i)["x"] for i in range(4)]
+    dev_x = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).cuda().view(torch.bfloat16)
+    x = dev_x(xs[0])
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    a = lay.act_buffers(m)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        lay.quantize(x, side)
+        lay.gemm(a, m, y, side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            lay.quantize(x, side)
+            lay.gemm(a, m, y, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    # eager references on separate buffers (the graph's own buffers belong to the capture)
+    other = w4.W4A4Linear(w4.prepare_weights(d["w"], lam, r, fmt, bf(ref["l1"]), bf(ref["l2"])), inv)
+    for i, xb in enumerate(xs[1:] + xs[:1]):
+        x.copy_(dev_x(xb))
+        y_eager = other(dev_x(xb))
+        torch.cuda.synchronize()
+        g.replay()
+        junk = other(dev_x(xs[(i + 2) % 4]))   # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {i} differs from the eager step"
+        if i == 3:   # xs[0] again: against the oracle
+            y_ref = O.linear(xs[0], inv, ref)["y"]
+            yb = O.bf16_bits_to_f32(y.view(torch.int16).cpu().numpy().view(np.uint16))
+            assert np.abs(yb - y_ref).max() <= 2.0 ** -7 * np.abs(y_ref).max()
+        del junk
+
+
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
 @pytest.mark.parametrize("case", [
     (2000, 512, 8440, 20, True),   # 8 x 33 = 264 tiles (more than the GPU runs at once), 8 groups
     (2000, 832, 8440, 20, True),   # 13 groups: the last ring round is partial
