@@ -481,9 +481,22 @@ def test_w8a8_largest_k():
 
 
 # ------------------------------------------------------------ the layer the library prepares itself
-@pytest.mark.parametrize("name", ["tiny", "flux_qkv"])
+def _check_weight_codes(prep, ref, N, K, fmt):
+    """The library's weight codes and scales, canonicalized, against the oracle's quantization."""
+    codes = w4.codes_to_canonical(prep["wq"], N, K, fmt)
+    scales = w4.scales_to_canonical(prep["wscale"], N, K, fmt)
+    if fmt == "int4_g64":
+        assert np.array_equal(codes, O.pack_int4(ref["cw"])) and np.array_equal(scales, O.f32_to_bf16_bits(ref["sw"]))
+    elif fmt == "mxfp4_b32":
+        assert np.array_equal(codes, O.pack_nibbles(ref["cw"])) and np.array_equal(scales, ref["sw"])
+    else:
+        assert np.array_equal(codes, ref["cw"]) and np.array_equal(scales, ref["sw"])
+
+
+@pytest.mark.parametrize("name,fmt", [("tiny", "int4_g64"), ("flux_qkv", "int4_g64"), ("tiny", "mxfp4_b32"),
+                                      ("tiny", "w8a8")])
 @pytest.mark.parametrize("refine", [0, 2])
-def test_library_prepared_layer(name, refine):
+def test_library_prepared_layer(name, fmt, refine):
     """The layer exactly as the bench builds it: λ from the library's own channel maxima, the
     library's own rank-r SVD (and, with `refine`, its iterative refinement of the split, §4.2),
     then both kernels. λ and 1/λ are bit-exact; the weight codes and scales are bit-exact against
@@ -493,7 +506,7 @@ def test_library_prepared_layer(name, refine):
     (LAPACK-SVD) layer, within 5% (the SVD is a different algorithm, so its factors are not
     elementwise comparable)."""
     d = synth.workload(name)
-    fmt, r, K, N = d["fmt"], d["rank"], d["K"], d["N"]
+    r, K, N = d["rank"], d["K"], d["N"]
     ax, aw = w4.column_absmax(d["x"]), w4.column_absmax(d["w"])
     lam, inv = w4.smooth_factors(ax, aw)
     lo, io = _smooth(d)
@@ -503,9 +516,8 @@ def test_library_prepared_layer(name, refine):
         assert prep["errors"][prep["iteration"]] == min(prep["errors"])
     l1, l2 = O.bf16_bits_to_f32(prep["l1"]), O.bf16_bits_to_f32(prep["l2"])
     ref = O.prepare_weights(d["w"], lam, r, fmt, l1=l1, l2=l2)
-    assert np.array_equal(w4.codes_to_canonical(prep["wq"], N, K, fmt), O.pack_int4(ref["cw"]))
-    assert np.array_equal(w4.scales_to_canonical(prep["wscale"], N, K, fmt), O.f32_to_bf16_bits(ref["sw"]))
-    print(f"[library prep] {name} M={d['M']} K={K} N={N} r={r} refine={refine}", flush=True)
+    _check_weight_codes(prep, ref, N, K, fmt)
+    print(f"[library prep] {name} {fmt} M={d['M']} K={K} N={N} r={r} refine={refine}", flush=True)
     g = gpu_layer(d, lam, inv, r, fmt, prep=prep, pad_cols=3)
     check_activation_side(d, inv, ref, fmt, g)
     check_y(g, O.linear(d["x"], inv, ref)["y"])
