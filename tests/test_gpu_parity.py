@@ -460,6 +460,51 @@ def test_mxfp4_large_grid_high_rank(r):
     assert np.all(g["y"][:, n:] == -7.0), "wrote outside the M x N block"
 
 
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
+def test_largest_operands(fmt):
+    """The largest activation operand the kernels' 32-bit offsets allow: rows_pad·K = 2^31 elements
+    (INT4, MXFP4; W8A8, whose one-byte codes must stay below 2^31 bytes, one row tile less) at
+    K 16384 with a ragged M, ragged N (320) with bias and rank 16. X repeats 512 seeded rows (the
+    host holds only those); every row of Y's first and last tiles, the rows around each 8192-row
+    boundary and random rows are compared with the oracle, and t on the same rows."""
+    K, N, r = 16384, 320, 16
+    rows_pad = (1 << 31) // K - (256 if fmt == "w8a8" else 0)
+    M = rows_pad - 100
+    base = synth.make_layer(512, K, N, n_outliers=16, outlier_scale=30.0, seed=77)
+    lam, inv = _smooth(base)
+    ref = oracle_weights(base, r, fmt, lam)
+    rng = np.random.default_rng(5)
+    bias = O.f32_to_bf16_bits(O.bf16_rne(rng.standard_normal(N).astype(np.float32)))
+    bf = O.f32_to_bf16_bits
+    lay = w4.W4A4Linear(w4.prepare_weights(base["w"], lam, r, fmt, bf(ref["l1"]), bf(ref["l2"])), inv, bias_bits=bias)
+    print(f"[largest operands] fmt={fmt} M={M} (rows_pad {rows_pad}) K={K} N={N} r={r}", flush=True)
+    xb = torch.from_numpy(np.ascontiguousarray(base["x"]).view(np.int16)).cuda()
+    x = xb[torch.arange(M, device="cuda") % 512].view(torch.bfloat16)       # row i = base row i % 512
+    y = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda")
+    a = lay.act_buffers(M)
+    lay.quantize(x)
+    lay.gemm(a, M, y)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 256), np.arange(M - 256, M),
+                                     (np.arange(8192, M, 8192)[:, None] + np.arange(-2, 2)).ravel(),
+                                     rng.choice(M, 64, replace=False)]))
+    rows = rows[(rows >= 0) & (rows < M)]
+    sel = torch.from_numpy(rows).cuda()
+    yb = O.bf16_bits_to_f32(y[sel].view(torch.int16).cpu().numpy().view(np.uint16))
+    xr = base["x"][rows % 512]
+    want = O.linear(xr, inv, ref, bias)
+    err = np.abs(yb.astype(np.float64) - want["y"].astype(np.float64)).max()
+    assert err <= TOL * np.abs(want["y"]).max(), f"max|dY| = {err}"
+    rp = (r + 15) // 16 * 16
+    t = a["xl1"][: rows_pad * rp].view(rows_pad, rp)[sel].cpu().numpy()
+    act = O.quantize_activations(xr, inv, ref["l1"], fmt)
+    terms = np.abs(O.bf16_rne(act["x_hat"]).astype(np.float64)) @ np.abs(ref["l1"].astype(np.float64))
+    assert np.all(np.abs(t[:, :r] - act["t"]) <= 2.0 * K * 2.0 ** -24 * terms + 1e-30), "t outside the fp32 bound"
+    del x, xb, y, a
+    lay._act.clear()
+    torch.cuda.empty_cache()
+
+
 def test_w8a8_largest_k():
     """W8A8 at the largest K whose int32 dot products cannot overflow (127² · 131072 < 2^31), with
     rows of near-full-scale codes so that the exact sums come close to the limit."""
