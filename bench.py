@@ -73,18 +73,24 @@ def new_flush(dev):
     return torch.empty(1 << 28, dtype=torch.float32, device=dev)
 
 
-def cold_run(parts, n, flush):
+def cold_run(parts, n, flush, read_flush=False):
     """`n` steps of the callables `parts` (run in order on the current stream). Before each step the
     flush buffer is overwritten (not timed); HIP events on the stream time every part. Returns the
     per-step, per-part times [n, len(parts)] in ms and the wall-clock seconds of the whole loop
-    (flushes included)."""
+    (flushes included). With `read_flush` the buffer is read instead (a sum over it): the caches are
+    as cold, but the MALL then holds clean lines, so the step does not pay for writing back the
+    flush's dirty ones."""
     import torch
     stream = torch.cuda.current_stream()
     out = np.zeros((n, len(parts)))
+    sink = torch.zeros((), dtype=torch.float32, device=flush.device)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(n):
-        flush.fill_(float(i & 7))
+        if read_flush:
+            sink.copy_(flush.sum())
+        else:
+            flush.fill_(float(i & 7))
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
         ev[0].record(stream)
         for k, f in enumerate(parts):
@@ -474,6 +480,8 @@ def main():
     g_avg = float(g_c.mean())   # the GEMM's average launch time over the timed steps
     # the warm view: back-to-back steps, inputs left in the MALL by the previous step
     warm_ms, tw = warm_run(parts, args.steps)
+    # cold caches without the write-back of the flush's dirty lines (a read sweep of the buffer)
+    tr = cold_run(parts, min(args.steps, 20), flush, read_flush=True)[0]
 
     ops = layer_ops(M, N, K, r)
     value = ops / (ms_step * 1e-3) / 1e12
@@ -496,6 +504,7 @@ def main():
                    "peak_frac_of_step": round(value / peak, 4)},
         "timing": {"ms_per_step_cold_median": round(ms_step, 5),
                    "ms_per_step_cold_p10_p90": [pct(step_c, 10), pct(step_c, 90)],
+                   "ms_per_step_cold_readflush_median": round(float(np.median(tr.sum(axis=1))), 5),
                    "ms_per_step_warm": round(warm_ms, 5),
                    "TOPS_warm": round(ops / (warm_ms * 1e-3) / 1e12, 2),
                    "wall_s_timed_loop_incl_flushes": round(wall, 4)},
@@ -509,6 +518,7 @@ def main():
         "kernels": {
             "quantize_act": {"ms_cold_median_p10_p90": [round(q_med, 5), pct(q_c, 10), pct(q_c, 90)],
                              "ms_warm_mean": round(float(tw[:, 0].mean()), 5),
+                             "ms_cold_readflush_median": pct(tr[:, 0], 50),
                              "algorithmic_bytes": qbytes,
                              "GB/s_cold": round(qbytes / (q_med * 1e-3) / 1e9, 1),
                              "hbm_frac_cold": round(qbytes / (q_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -516,6 +526,7 @@ def main():
                              "frac_of_copy_cold": round(qbytes / (q_med * 1e-3) / 1e9 / copy_gbs, 4)},
             "gemm": {"ms_cold_median_p10_p90": [pct(g_c, 50), pct(g_c, 10), pct(g_c, 90)],
                      "ms_cold_mean": round(g_avg, 5), "ms_warm_mean": round(float(tw[:, 1].mean()), 5),
+                     "ms_cold_readflush_median": pct(tr[:, 1], 50),
                      "TOPS_cold": round(ops / (np.median(g_c) * 1e-3) / 1e12, 2)},
         },
     }
