@@ -16,7 +16,10 @@
  * Conventions
  *  - Ownership: the caller allocates and frees every buffer; host buffers are ordinary arrays,
  *    device buffers are device memory (e.g. from torch). The library never allocates device
- *    memory, never synchronizes a stream and keeps no mutable global state.
+ *    memory, never synchronizes a stream and keeps no mutable global state, with two exceptions
+ *    described at their calls: the GELU table that the first GELU call on a device fills in the
+ *    library's device data (waiting on that call's stream), and the fixed device scratch array of
+ *    the no-allocation MLP call.
  *  - bf16 tensors are passed as uint16_t bit patterns. Row-major everywhere.
  *  - Library layouts: codes and scales of activations and weights, and the low-rank factors, use
  *    the private layouts described at w4a4_buffer_sizes(). Rows (M of X, N of W) are padded to a
