@@ -75,15 +75,48 @@ __device__ __forceinline__ float gelu32(float y) {
   return (0.5f * y) * (1.0f + e);
 }
 
-// The GELU of a bf16 input rounded to bf16 takes one of 65536 values: this table holds
-// bf16(gelu32(x)) for every bf16 bit pattern x, filled once per device by gelu_table_kernel with
-// the function above, so a lookup returns exactly what evaluating gelu32 would.
-static __device__ uint16_t gelu_tab[65536];
+// The GELU of a bf16 input rounded to bf16 is a function of the input's 16 bits. The kernels
+// take it from a table of bf16(gelu32(x)) over the inputs with 2^-20 <= |x| < 256 (biased exponent
+// 107..134, both signs: 2 x 28 x 128 entries, 14 KB) that they keep in LDS, and evaluate gelu32
+// itself for every other input (zeros, tiny and huge magnitudes, Inf and NaN: rare in a layer's
+// output); either way the value is exactly what evaluating gelu32 gives. The table, laid out
+// [sign][exponent - 107][mantissa], is filled once per device by gelu_table_kernel with the
+// function above and copied into each block's LDS.
+constexpr int GELU_E0 = 107, GELU_NE = 28;                 // exponents 107 .. 134
+constexpr int GELU_SIGN = GELU_NE * 128;                   // entries per sign
+constexpr int GELU_TAB = 2 * GELU_SIGN;                    // 7168 entries
+constexpr int GELU_SLOTS = GELU_TAB * 2 / 16;              // 896 16-byte LDS slots
+static __device__ __attribute__((aligned(16))) uint16_t gelu_tab[GELU_TAB];
 __global__ void gelu_table_kernel() {
-  const uint32_t x = blockIdx.x * 256 + threadIdx.x;
-  gelu_tab[x] = (uint16_t)bf16_rne(gelu32(bf16f(x)));
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= GELU_TAB) return;
+  const uint32_t x = (uint32_t)(i / GELU_SIGN) << 15 | (uint32_t)(GELU_E0 + (i % GELU_SIGN) / 128) << 7 | (uint32_t)(i % 128);
+  gelu_tab[i] = (uint16_t)bf16_rne(gelu32(bf16f(x)));
 }
-__device__ __forceinline__ uint32_t gelu_bf16(uint32_t bits) { return gelu_tab[bits & 0xFFFFu]; }
+// offset of bf16 input `b` in the table's magnitude range, or >= GELU_SIGN outside it
+__device__ __forceinline__ uint32_t gelu_off(uint32_t b) { return (b & 0x7FFFu) - (uint32_t)(GELU_E0 << 7); }
+// bf16(GELU(b)) from the LDS table `tab` for an input in its range (gelu_off(b) < GELU_SIGN)
+__device__ __forceinline__ uint32_t gelu_tab_lookup(uint32_t b, const uint16_t* tab) {
+  return tab[gelu_off(b) + (b >> 15) * (uint32_t)GELU_SIGN];
+}
+// bf16(GELU(b)) for any input
+__device__ __forceinline__ uint32_t gelu_any(uint32_t b, const uint16_t* tab) {
+  return gelu_off(b) < (uint32_t)GELU_SIGN ? gelu_tab_lookup(b, tab) : bf16_rne(gelu32(bf16f(b)));
+}
+// N inputs at once: the plain lookups when every input of the lane is in the table's range
+template <int N>
+__device__ __forceinline__ void gelu_n(uint32_t (&b)[N], const uint16_t* tab) {
+  bool all_in = true;
+#pragma unroll
+  for (int e = 0; e < N; ++e) all_in &= gelu_off(b[e]) < (uint32_t)GELU_SIGN;
+  if (all_in) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) b[e] = gelu_tab_lookup(b[e], tab);
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e) b[e] = gelu_any(b[e], tab);
+  }
+}
 
 // INT4 codes of one group row held by four lanes (lane bits 4-5 = kc, 16 values each): s =
 // bf16(max|X̂| / 7) (0 below 2^-126), q = rint(X̂ · (1/s)) (|q| <= 7 by the symmetric scale). The fp32
@@ -183,14 +216,14 @@ __device__ __forceinline__ void scale_pair(const float (&ua)[16], const float (&
 }
 
 template <bool GELU_IN>
-__device__ __forceinline__ void unpack16(const v4i (&xv)[2], float (&u)[16]) {
+__device__ __forceinline__ void unpack16(const v4i (&xv)[2], float (&u)[16], const uint16_t* gtab) {
   uint32_t bits[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const uint32_t w = (uint32_t)xv[e >> 3][(e >> 1) & 3];
     bits[e] = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-    if (GELU_IN) bits[e] = gelu_bf16(bits[e]);  // the 16 table reads go out together
   }
+  if constexpr (GELU_IN) gelu_n(bits, gtab);  // the 16 table reads go out together
 #pragma unroll
   for (int e = 0; e < 16; ++e) u[e] = bf16f(bits[e]);
 }
@@ -198,16 +231,18 @@ __device__ __forceinline__ void unpack16(const v4i (&xv)[2], float (&u)[16]) {
 // X̂ = fp32(x · (1/λ)), one fp32 multiply per value (no contraction: nothing to fuse)
 template <bool GELU_IN>
 __device__ __forceinline__ void smooth_pair(const v4i (&xva)[2], const v4i (&xvb)[2], uint32_t ila, uint32_t ilb,
-                                            float (&xa)[16], float (&xb)[16]) {
+                                            float (&xa)[16], float (&xb)[16], const uint16_t* gtab) {
   float ua[16], ub[16];
-  unpack16<GELU_IN>(xva, ua);
-  unpack16<GELU_IN>(xvb, ub);
+  unpack16<GELU_IN>(xva, ua, gtab);
+  unpack16<GELU_IN>(xvb, ub, gtab);
   scale_pair(ua, ub, ila, ilb, xa, xb);
 }
 
-// LDS bytes of one block: 1/λ (16 B slots), L1 rows of RP rank columns padded by one slot, in
-// whole 64-slot DMA instructions
-constexpr int qa_lds_slots(int rp, int gs) { return (gs * 16 + rp * (gs * 8 + 1) + 63) / 64 * 64; }
+// LDS of one block in 16-byte slots: 1/λ, L1 rows of RP rank columns padded by one slot, and with
+// the GELU on load its table, in whole 64-slot DMA instructions
+constexpr int qa_lds_slots(int rp, int gs, bool gelu = false) {
+  return (gs * 16 + rp * (gs * 8 + 1) + (gelu ? GELU_SLOTS : 0) + 63) / 64 * 64;
+}
 
 template <int FMT, int NT, bool GELU_IN = false>  // NT = rank_pad / 16 (0 when there is no low-rank branch)
 __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
@@ -228,14 +263,17 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
   // ---- 1. 1/λ and L1 rows of the slice -> LDS. Slot s (16 B) of the block's LDS: s < 16 ng are
   // 1/λ; then rank row c uses slots [16 ng + c (8 ng + 1), +8 ng + 1) for k = 64 g0 .. 64 (g0 + ng),
   // the last one padding. Each DMA instruction fills 64 consecutive slots.
-  const int n_il = ng * 16, l1_row = ng * 8 + 1, n_all = n_il + RP * l1_row;
+  // With the GELU on load its table follows: slots [n_l1, n_l1 + GELU_SLOTS).
+  const int n_il = ng * 16, l1_row = ng * 8 + 1, n_l1 = n_il + RP * l1_row;
+  const int n_all = n_l1 + (GELU_IN ? GELU_SLOTS : 0);
   for (int s0 = wave * 64; s0 < n_all; s0 += QA_WAVES * 64) {
     const int s = s0 + lane;
     const void* src = inv_lambda + (size_t)g0 * W4A4_GROUP + 4 * min(s, n_il - 1);
-    if (NT > 0 && s >= n_il && s < n_all) {
+    if (NT > 0 && s >= n_il && s < n_l1) {
       const int c = (s - n_il) / l1_row, j = (s - n_il) % l1_row;
       src = l1t + (size_t)c * K + (size_t)g0 * W4A4_GROUP + 8 * (j < ng * 8 ? j : 0);
     }
+    if (GELU_IN && s >= n_l1) src = gelu_tab + 8 * min(s - n_l1, GELU_SLOTS - 1);
     __builtin_amdgcn_global_load_lds(src, smem + 16 * s0, 16, 0, 0);
   }
 
@@ -263,6 +301,7 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
   const uint32_t* s_il = reinterpret_cast<const uint32_t*>(smem);
   const uint8_t* s_l1 = smem + 16 * n_il;
   const int l1_stride = 16 * l1_row;
+  const uint16_t* s_gelu = reinterpret_cast<const uint16_t*>(smem + 16 * n_l1);
 
   // the outputs as buffers: a store whose offset lies past the buffer is dropped, so a pair without
   // its second group needs no branch
@@ -303,7 +342,7 @@ __global__ __launch_bounds__(QA_WAVES * 64) void quantize_act_kernel(
     const uint32_t ila = s_il[i * W4A4_GROUP + kc * 16 + r];
     const uint32_t ilb = s_il[min(i + 1, ng - 1) * W4A4_GROUP + kc * 16 + r];
     float xa[16], xb[16];  // group gb is all zeros when the slice has no such group
-    smooth_pair<GELU_IN>(xv[i], xv[i + 1], ila, ilb, xa, xb);
+    smooth_pair<GELU_IN>(xv[i], xv[i + 1], ila, ilb, xa, xb, s_gelu);
     if constexpr (FMT == W4A4_FMT_INT4_G64) {
       float ma = 0.f, mb = 0.f;
 #pragma unroll
@@ -481,9 +520,9 @@ struct SlotSet {
 
 template <int NT2>
 __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8_t* stage, SlotSet slots,
-                                                    const GeluQuantArgs& fa, const uint16_t* bias, int M, int N,
-                                                    int m_pad, int m0, int n0, int tn, int wm, int wn, int wave,
-                                                    int lane);
+                                                    const uint16_t* gtab, const GeluQuantArgs& fa,
+                                                    const uint16_t* bias, int M, int N, int m_pad, int m0, int n0,
+                                                    int tn, int wm, int wn, int wave, int lane);
 
 // FUSE < 0: the plain GEMM (fa unused). FUSE >= 0 (INT4 only): fc1 of the MLP with fc2's
 // activation side in the epilogue, FUSE = fc2's rank_pad / 16; Y may then be NULL.
@@ -834,6 +873,17 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   }
   wait_vmcnt<0>();  // no LDS DMA may outlive the block
   __builtin_amdgcn_s_barrier();  // every wave is done with the ring (and its DMA has landed)
+  const uint16_t* gtab = reinterpret_cast<const uint16_t*>(ring[4]);
+  if constexpr (FUSE >= 0) {  // the GELU table into slot 4, idle from here on (1 KB per instruction)
+    static_assert(GELU_SLOTS * 16 <= (int)sizeof(I4Slot) && GELU_SLOTS <= 16 * 64, "GELU table fits slot 4");
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = wave + 8 * q;
+      if (c * 64 < GELU_SLOTS)
+        __builtin_amdgcn_global_load_lds(gelu_tab + 8 * min(c * 64 + lane, GELU_SLOTS - 1),
+                                         reinterpret_cast<uint8_t*>(ring[4]) + 1024 * c, 16, 0, 0);
+    }
+  }
   // the eight waves' staging areas: wave w uses half (w & 1) of slot w / 2
   SlotSet slots;
 #pragma unroll
@@ -847,7 +897,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     store_y(acc, stage, bias, Y, ldy, M, N, m0 + wm * 128, n0 + wn * 64, lane);
   } else {
     if (Y) store_y(acc, stage, bias, Y, ldy, M, N, m0 + wm * 128, n0 + wn * 64, lane);  // for checking
-    gelu_quant_epilogue<FUSE>(acc, stage, slots, fa, bias, M, N, m_pad, m0, n0, tn, wm, wn, wave, lane);
+    gelu_quant_epilogue<FUSE>(acc, stage, slots, gtab, fa, bias, M, N, m_pad, m0, n0, tn, wm, wn, wave, lane);
   }
 }
 
@@ -860,9 +910,9 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
 // block rows then sum their partials through LDS in a fixed order into this tile's plane.
 template <int NT2>
 __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8_t* stage, SlotSet slots,
-                                                    const GeluQuantArgs& fa, const uint16_t* bias, int M, int N,
-                                                    int m_pad, int m0, int n0, int tn, int wm, int wn, int wave,
-                                                    int lane) {
+                                                    const uint16_t* gtab, const GeluQuantArgs& fa,
+                                                    const uint16_t* bias, int M, int N, int m_pad, int m0, int n0,
+                                                    int tn, int wm, int wn, int wave, int lane) {
   constexpr int RP2 = NT2 * 16, NT2A = NT2 > 0 ? NT2 : 1;
   const int lr = lane & 31, lh = lane >> 5;  // 32x32 MFMA output layout
   const int r = lane & 15, kc = lane >> 4;   // activation-kernel layout
@@ -896,6 +946,8 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
 #pragma unroll
     for (int p = 0; p < 8; ++p) tacc[p][c] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+  wait_vmcnt<0>();               // this wave's copies of the GELU table have landed
+  __builtin_amdgcn_s_barrier();  // and every other wave's
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     // the half's 64 GELU values per lane: every table read issued before the first is used (the
@@ -908,9 +960,10 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
           const uint32_t y = pack_bf16x2(acc[2 * half + ii][j][v] + bcol[j], acc[2 * half + ii][j][v + 1] + bcol[j]);
-          gx[ii][j][v] = gelu_bf16(y);
-          gx[ii][j][v + 1] = gelu_bf16(y >> 16);
+          gx[ii][j][v] = y & 0xFFFFu;
+          gx[ii][j][v + 1] = y >> 16;
         }
+    gelu_n(*reinterpret_cast<uint32_t(*)[64]>(&gx[0][0][0]), gtab);
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -1200,7 +1253,7 @@ hipError_t ensure_gelu_table(hipStream_t st) {
   try {
     std::lock_guard<std::mutex> lock(mu);
     if (ready[dev].load(std::memory_order_relaxed)) return hipSuccess;
-    hipLaunchKernelGGL(gelu_table_kernel, dim3(65536 / 256), dim3(256), 0, st);
+    hipLaunchKernelGGL(gelu_table_kernel, dim3((GELU_TAB + 255) / 256), dim3(256), 0, st);
     e = hipGetLastError();
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e == hipSuccess) ready[dev].store(true, std::memory_order_release);
@@ -1214,7 +1267,7 @@ template <int FMT, int NT, bool GELU_IN = false>
 hipError_t launch_qa(const uint16_t* X, int M, int K, int ldx, const float* il, const uint16_t* l1t, int m_pad,
                      uint8_t* xq, void* xs, float* xl1, hipStream_t st) {
   const int gs = qa_group_slice(M, K), nsl = qa_slices(M, K);
-  const size_t lds = 16 * (size_t)qa_lds_slots(NT * 16, gs);
+  const size_t lds = 16 * (size_t)qa_lds_slots(NT * 16, gs, GELU_IN);
   if (lds > 65536) {  // large ranks: allow the block more than 64 KB of dynamic LDS
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&quantize_act_kernel<FMT, NT, GELU_IN>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
