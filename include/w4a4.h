@@ -242,9 +242,10 @@ w4a4_status_t w4a4_lowrank_linear(const uint8_t* xq, const void* xscale, const f
  * 7.1.28, 1 - (1 + a1 x + ... + a6 x^6)^-16, |error| <= 3e-7, evaluated one IEEE fp32 operation at a
  * time (Horner from a6, the 16th power by four squarings, correctly rounded division), so that
  * the bf16 rounding of X2 = bf16(GELU(Y1)) is reproducible on a host. The first GELU call on a
- * device evaluates it once for every bf16 input into a table in the library's device data (on the
- * call's stream, waiting for it; not possible during stream capture, where it returns
- * W4A4_ERR_HIP and is retried by the next call); later calls look the values up.
+ * device evaluates it once for the bf16 inputs with 2^-20 <= |x| < 256 into a 14 KB table in the
+ * library's device data (on the call's stream, waiting for it; not possible during stream capture,
+ * where it returns W4A4_ERR_HIP and is retried by the next call); the kernels look those values up
+ * and evaluate the function for every other input, with identical results.
  *
  * Consumer side: w4a4_quantize_act (INT4 only) applied to X = bf16(GELU(Y)) of a producer's bf16
  * output Y [M][ldy] (device; K <= ldy <= 2^26, ldy % 8 == 0); every other argument as for
