@@ -615,21 +615,20 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   const int a_off = sw_off32(arow0, lh), b_off = sw_off32(bcol0, lh);
 
   // low-rank up projection first: acc = bf16(t) · L2 over k = rank index (32x32x16 bf16 MFMA); the
-  // 4-bit groups then accumulate on top. Up to rank 32 the block's t tile (256 rows x 32 fp32 =
-  // 32 KB, read by four waves each) is copied once into the last two ring slots by the LDS DMA path
-  // before the ring's first groups, and the L2 operands are loaded before them too; all of it
-  // lands under the prologue's wait for group 0 and the MFMAs run right after it. Larger ranks
-  // load t directly, 32 ranks at a time.
+  // 4-bit groups then accumulate on top. Up to rank 48 the block's t tile (256 rows x rank_pad
+  // fp32, at most 48 KB, read by four waves each) is copied once into the last two ring slots by
+  // the LDS DMA path before the ring's first groups, and the L2 operands are loaded before them
+  // too; all of it lands under the prologue's wait for group 0 and the MFMAs run right after it.
+  // Larger ranks load t directly, 32 ranks at a time.
   constexpr int RP = NTR * 16, KS = 2;  // up to two 16-rank MFMA K-steps per batch of loads
-  constexpr bool T_LDS = NTR > 0 && NTR <= 2;
+  constexpr bool T_LDS = NTR > 0 && NTR <= 3;
   constexpr int TROWB = RP * 4;          // bytes of one t row
-  static_assert(256 * 32 * 4 <= 2 * 16384 && 16384 <= (int)sizeof(I4Slot), "t tile fits the last two slots");
-  // t row r of the block lives at byte r * TROWB of the tile: the first 16 KB in slot 6, the rest
-  // in slot 7
+  constexpr int TSPLIT = 128 * TROWB;    // rows 0..127 of the tile in slot 4, rows 128..255 in slot 5
+  static_assert(!T_LDS || TSPLIT <= (int)offsetof(I4Slot, z), "half the t tile fits a slot below its zero words");
   auto t_row_ptr = [&](int r) -> const uint8_t* {
     const int byte = r * TROWB;
-    return byte < 16384 ? reinterpret_cast<const uint8_t*>(ring[I4_RING - 2]) + byte
-                        : reinterpret_cast<const uint8_t*>(ring[I4_RING - 1]) + (byte - 16384);
+    return byte < TSPLIT ? reinterpret_cast<const uint8_t*>(ring[I4_RING - 2]) + byte
+                         : reinterpret_cast<const uint8_t*>(ring[I4_RING - 1]) + (byte - TSPLIT);
   };
   v4i LB[KS][2];
   float4 tv[KS][I4_MT][2];
@@ -651,16 +650,17 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
       }
     }
   };
-  // t from its LDS tile: one asm block with every read and its own wait (the compiler's LDS-DMA
-  // tracking cannot tell slots 6/7 from the ring groups still in flight and would wait for all of
-  // them). Lane address of tile row i: the row's byte in the tile plus 32 lh (ranks 8 lh ..).
-  auto t_from_lds = [&]() {
+  // t from its LDS tile, ranks k0 .. k0 + 31 (one or two 16-rank K-steps): one asm block with
+  // every read and its own wait (the compiler's LDS-DMA tracking cannot tell slots 4/5 from the
+  // ring groups still in flight and would wait for all of them). Lane address of tile row i: the
+  // row's byte in the tile plus 4 k0 + 32 lh (ranks k0 + 8 lh ..).
+  auto t_from_lds = [&](int k0) {
     typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
     uint32_t ad[I4_MT];
 #pragma unroll
     for (int i = 0; i < I4_MT; ++i)
-      ad[i] = (uint32_t)(uintptr_t)(lds_cptr)t_row_ptr(wm * 128 + i * 32 + lr) + 32 * lh;
-    if constexpr (NTR == 2) {
+      ad[i] = (uint32_t)(uintptr_t)(lds_cptr)t_row_ptr(wm * 128 + i * 32 + lr) + 4 * k0 + 32 * lh;
+    if (RP - k0 >= 32) {
       asm volatile(
           "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:16\n\t"
           "ds_read_b128 %2, %16 offset:64\n\tds_read_b128 %3, %16 offset:80\n\t"
@@ -677,7 +677,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
             "=&v"(tv[0][3][0]), "=&v"(tv[0][3][1]), "=&v"(tv[1][3][0]), "=&v"(tv[1][3][1])
           : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
           : "memory");
-    } else if constexpr (NTR == 1) {
+    } else {
       asm volatile(
           "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\t"
           "ds_read_b128 %2, %9\n\tds_read_b128 %3, %9 offset:16\n\t"
@@ -707,16 +707,23 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     }
   };
   if (NTR > 0) lr_load(0);
+  v4i LBn[2] = {};  // staged t above rank 32: the L2 operands of ranks 32 .. 47, loaded up front too
+  if constexpr (T_LDS && NTR > 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      LBn[j] = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 64 + j * 32 + lr) * RP + 32 + 8 * lh);
+  }
   if (T_LDS) {  // t tile -> the last two slots: TBYTES / 8 bytes per wave, 1 KB per DMA instruction
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     const __amdgpu_buffer_rsrc_t t_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(xl1 + (size_t)m0 * RP), 0, (m_pad - m0) * TROWB, RSRC_W3);
     constexpr int TCHUNK = 256 * TROWB / 8;
+    static_assert(TCHUNK % 1024 == 0 && TSPLIT % 1024 == 0, "whole DMA instructions, none across the split");
 #pragma unroll
     for (int q = 0; q < TCHUNK / 1024; ++q) {
-      const int off = wave * TCHUNK + q * 1024;  // chunks never straddle the 16 KB split
-      uint8_t* dst = off < 16384 ? reinterpret_cast<uint8_t*>(ring[I4_RING - 2]) + off
-                                 : reinterpret_cast<uint8_t*>(ring[I4_RING - 1]) + (off - 16384);
+      const int off = wave * TCHUNK + q * 1024;
+      uint8_t* dst = off < TSPLIT ? reinterpret_cast<uint8_t*>(ring[I4_RING - 2]) + off
+                                  : reinterpret_cast<uint8_t*>(ring[I4_RING - 1]) + (off - TSPLIT);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr_t)dst, 16, 16 * lane, off, 0, 0);
     }
   }
@@ -731,11 +738,17 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   wait_vmcnt<DMA_PER_GROUP * (I4_RING - 3)>();
   __builtin_amdgcn_s_barrier();
   if (NTR > 0) {
-    if (T_LDS) t_from_lds();
+    if (T_LDS) t_from_lds(0);
     lr_mfma(0);
 #pragma unroll
     for (int k0 = 32; k0 < RP; k0 += 32) {
-      lr_load(k0);
+      if constexpr (T_LDS) {
+        LB[0][0] = LBn[0];
+        LB[0][1] = LBn[1];
+        t_from_lds(k0);
+      } else {
+        lr_load(k0);
+      }
       lr_mfma(k0);
     }
   }
