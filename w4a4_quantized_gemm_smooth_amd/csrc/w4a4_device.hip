@@ -1146,7 +1146,13 @@ __global__ __launch_bounds__(MX_THREADS, 2) void gemm_mx_small_kernel(
   constexpr int RP = NTR * 16;
   v4i LB[2][2];
   float4 tv[2][MX_MT][2];
-  auto lr_load = [&](int k0) {
+  // Up to rank 32 the block's t tile (128 rows x rank_pad fp32, at most 16 KB) is copied by the
+  // LDS DMA path into slots 6 and 7 (rows 0..63 and 64..127), idle until the main loop's first
+  // copies; larger ranks load t directly.
+  constexpr bool T_LDS = NTR > 0 && NTR <= 2;
+  constexpr int TROWB = RP * 4;
+  static_assert(!T_LDS || 64 * TROWB <= (int)sizeof(MxSlot), "half the t tile fits a slot");
+  auto lr_load = [&](int k0) {  // L2 operands, and t when it is not staged in LDS
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int kk = k0 + 16 * s;
@@ -1154,12 +1160,47 @@ __global__ __launch_bounds__(MX_THREADS, 2) void gemm_mx_small_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         LB[s][j] = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + bcol0 + j * 32) * RP + kk + 8 * lh);
+      if (!T_LDS) {
 #pragma unroll
-      for (int i = 0; i < MX_MT; ++i) {
-        const float* tp = xl1 + (size_t)(m0 + arow0 + i * 32) * RP + kk + 8 * lh;
-        tv[s][i][0] = *reinterpret_cast<const float4*>(tp);
-        tv[s][i][1] = *reinterpret_cast<const float4*>(tp + 4);
+        for (int i = 0; i < MX_MT; ++i) {
+          const float* tp = xl1 + (size_t)(m0 + arow0 + i * 32) * RP + kk + 8 * lh;
+          tv[s][i][0] = *reinterpret_cast<const float4*>(tp);
+          tv[s][i][1] = *reinterpret_cast<const float4*>(tp + 4);
+        }
       }
+    }
+  };
+  // t from its LDS tile: one asm block with every read and its own wait (the compiler's LDS-DMA
+  // tracking cannot tell slots 6/7 from the ring groups still in flight and would wait for all of
+  // them). Lane address of tile row i: the row's byte in its slot plus 32 lh (ranks 8 lh ..).
+  auto t_from_lds = [&]() {
+    typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
+    uint32_t ad[MX_MT];
+#pragma unroll
+    for (int i = 0; i < MX_MT; ++i) {
+      const int r = arow0 + i * 32;  // wm * 64 + 32 i + lr: slot 6 for wm == 0, slot 7 for wm == 1
+      const uint8_t* slot = reinterpret_cast<const uint8_t*>((r >> 6) ? ring[7] : ring[6]);
+      ad[i] = (uint32_t)(uintptr_t)(lds_cptr)(slot + (r & 63) * TROWB) + 32 * lh;
+    }
+    if constexpr (NTR == 2) {
+      asm volatile(
+          "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\t"
+          "ds_read_b128 %2, %8 offset:64\n\tds_read_b128 %3, %8 offset:80\n\t"
+          "ds_read_b128 %4, %9\n\tds_read_b128 %5, %9 offset:16\n\t"
+          "ds_read_b128 %6, %9 offset:64\n\tds_read_b128 %7, %9 offset:80\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(tv[0][0][0]), "=&v"(tv[0][0][1]), "=&v"(tv[1][0][0]), "=&v"(tv[1][0][1]),
+            "=&v"(tv[0][1][0]), "=&v"(tv[0][1][1]), "=&v"(tv[1][1][0]), "=&v"(tv[1][1][1])
+          : "v"(ad[0]), "v"(ad[1])
+          : "memory");
+    } else if constexpr (NTR == 1) {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\t"
+          "ds_read_b128 %2, %5\n\tds_read_b128 %3, %5 offset:16\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(tv[0][0][0]), "=&v"(tv[0][0][1]), "=&v"(tv[0][1][0]), "=&v"(tv[0][1][1])
+          : "v"(ad[0]), "v"(ad[1])
+          : "memory");
     }
   };
   auto lr_mfma = [&](int k0) {
@@ -1178,11 +1219,25 @@ __global__ __launch_bounds__(MX_THREADS, 2) void gemm_mx_small_kernel(
     }
   };
   if (NTR > 0) lr_load(0);
+  if constexpr (T_LDS) {  // t tile -> slots 6 and 7: 16 * TROWB bytes per wave, 1 KB per DMA instruction
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+    const __amdgpu_buffer_rsrc_t t_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(xl1 + (size_t)m0 * RP), 0, (m_pad - m0) * TROWB, RSRC_W3);
+    constexpr int TCHUNK = 128 * TROWB / 4;  // wave w: rows 32 w .. 32 w + 31
+    static_assert(TCHUNK % 1024 == 0, "whole DMA instructions");
+#pragma unroll
+    for (int q = 0; q < TCHUNK / 1024; ++q) {
+      const int off = wave * TCHUNK + q * 1024;  // byte of the tile; rows 0..63 in slot 6
+      uint8_t* dst = reinterpret_cast<uint8_t*>(off >= 64 * TROWB ? ring[7] : ring[6]) + (off % (64 * TROWB));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr_t)dst, 16, 16 * lane, off, 0, 0);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < MX_NS - 2; ++s) dma(s, ring[s]);
   wait_vmcnt<3 * (MX_NS - 3)>();  // the low-rank operands and group 0 have landed
   __builtin_amdgcn_s_barrier();
   if (NTR > 0) {
+    if constexpr (T_LDS) t_from_lds();
     lr_mfma(0);
 #pragma unroll
     for (int k0 = 32; k0 < RP; k0 += 32) {  // larger ranks: later batches wait for their loads
