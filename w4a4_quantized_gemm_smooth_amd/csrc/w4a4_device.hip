@@ -1053,7 +1053,8 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
         float4 sum = float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {  // the four column waves of these rows, in order
-          const float* src = reinterpret_cast<const float*>(slots.s[4 * wr + w]);
+          // (a select between constant indices: a run-time index would put the array in scratch)
+          const float* src = reinterpret_cast<const float*>(wr ? slots.s[4 + w] : slots.s[w]);
           const float4 v = *reinterpret_cast<const float4*>(src + lrow * RP2 + 4 * q);
           sum.x += v.x;
           sum.y += v.y;
