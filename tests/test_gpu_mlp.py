@@ -142,6 +142,34 @@ def test_producer_side_fusion_without_y1():
     assert torch.equal(a2b["xq"], codes) and torch.equal(a2b["xscale"], scales) and torch.equal(a2b["xl1"], t)
 
 
+def test_consumer_side_strided_producer_output():
+    """fc2's activation kernel reading fc1's output through a row stride above K (Y1 a column slice
+    of a wider matrix, the extra columns holding values that must not be read): codes, scales and t2
+    bit-identical to the contiguous call."""
+    m, k, r = 200, 384, 24
+    rng = np.random.default_rng(12)
+    y_bits = O.f32_to_bf16_bits(O.bf16_rne((rng.standard_normal((m, k)) * 3).astype(np.float32)))
+    print(f"[strided Y1] M={m} K={k} ldy={k + 136} r={r}", flush=True)
+    y = torch.from_numpy(np.ascontiguousarray(y_bits).view(np.int16)).cuda().view(torch.bfloat16)
+    wide = torch.full((m, k + 136), -2.0e4, dtype=torch.bfloat16, device="cuda")
+    wide[:, :k] = y
+    ys = wide[:, :k]
+    inv = torch.from_numpy((rng.uniform(0.5, 2.0, k)).astype(np.float32)).cuda()
+    l1t = torch.from_numpy(O.f32_to_bf16_bits(O.bf16_rne((rng.standard_normal((32, k)) * 0.05).astype(np.float32)))
+                           .view(np.int16)).cuda()
+    sz = w4.buffer_sizes(m, r, k, r)
+    outs = []
+    for yin in (y, ys):
+        xq = torch.zeros(sz["xq"], dtype=torch.uint8, device="cuda")
+        xs = torch.zeros(sz["xscale"], dtype=torch.uint8, device="cuda")
+        xl1 = torch.zeros(sz["xl1"] // 4, dtype=torch.float32, device="cuda")
+        w4.gelu_quantize_act(yin, inv, l1t, r, "int4_g64", xq, xs, xl1)
+        torch.cuda.synchronize()
+        outs.append((xq.cpu(), xs.cpu(), xl1[: sz["m_pad"] * sz["rank_pad"]].cpu()))
+    for name, u, v in zip(("codes", "scales", "t2"), outs[0], outs[1]):
+        assert torch.equal(u, v), f"{name} differ with a row stride above K"
+
+
 def test_gelu_of_every_finite_bf16_input():
     """The device GELU on every finite bf16 pattern (65280 of them, as a 510 x 128 fc1 output) through
     fc2's activation kernel with 1/λ₂ = 1 and L1₂ the 128 x 128 identity (rank 128): then

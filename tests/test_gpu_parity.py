@@ -235,6 +235,43 @@ def test_deterministic_and_stream():
 
 
 @pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
+def test_strided_activations(fmt):
+    """X as a column slice of a wider matrix (row stride ldx = K + 72 elements, the extra columns
+    filled with large values that must not be read): codes, scales, t and Y bit-identical to the
+    same rows passed contiguously."""
+    m, k, n, r = 333, 448, 264, 20
+    d = synth.make_layer(m, k, n, n_outliers=5, outlier_scale=30.0, seed=31)
+    lam, inv = _smooth(d)
+    ref = oracle_weights(d, r, fmt, lam)
+    bf = lambda a: O.f32_to_bf16_bits(a)
+    lay = w4.W4A4Linear(w4.prepare_weights(d["w"], lam, r, fmt, bf(ref["l1"]), bf(ref["l2"])), inv)
+    print(f"[strided X] fmt={fmt} M={m} K={k} ldx={k + 72} N={n} r={r}", flush=True)
+    x = torch.from_numpy(np.ascontiguousarray(d["x"]).view(np.int16)).cuda().view(torch.bfloat16)
+    wide = torch.full((m, k + 72), 3.0e4, dtype=torch.bfloat16, device="cuda")
+    wide[:, :k] = x
+    xs = wide[:, :k]
+    assert xs.stride(0) == k + 72 and xs.stride(1) == 1
+    outs = []
+    for xin in (x, xs):
+        sz = w4.buffer_sizes(m, n, k, r, fmt)
+        a = dict(xq=torch.zeros(sz["xq"], dtype=torch.uint8, device="cuda"),
+                 xscale=torch.zeros(sz["xscale"], dtype=torch.uint8, device="cuda"),
+                 xl1=torch.zeros(sz["xl1"] // 4, dtype=torch.float32, device="cuda"))
+        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        w4.quantize_act(xin, lay.inv_lambda, lay.l1t, r, fmt, a["xq"], a["xscale"], a["xl1"])
+        lay.gemm(a, m, y)
+        torch.cuda.synchronize()
+        mp, rp = sz["m_pad"], sz["rank_pad"]
+        outs.append((a["xq"].cpu(), a["xscale"][: sz["xscale"] if fmt != "w8a8" else mp * 4].cpu(),
+                     a["xl1"][: mp * rp].cpu(), y.cpu()))
+    for name, u, v in zip(("codes", "scales", "t", "y"), outs[0], outs[1]):
+        assert torch.equal(u, v), f"{name} differ with a row stride above K"
+    y_ref = O.linear(d["x"], inv, ref)["y"]
+    yb = O.bf16_bits_to_f32(outs[1][3].view(torch.int16).numpy().view(np.uint16))
+    assert np.abs(yb - y_ref).max() <= TOL * np.abs(y_ref).max()
+
+
+@pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
 def test_graph_capture_and_replay(fmt):
     """The layer step (activation side, then the GEMM) captured once in a HIP graph: the library's
     launches allocate nothing and clear nothing, so the graph replays it. Three replays, each on new
