@@ -271,6 +271,45 @@ def test_strided_activations(fmt):
     assert np.abs(yb - y_ref).max() <= TOL * np.abs(y_ref).max()
 
 
+def test_concurrent_host_threads():
+    """Two host threads, each with its own stream, layer (INT4 and MXFP4) and buffers, call both
+    kernels eight times at once; every result is bit-identical to the same call made alone."""
+    import threading
+    jobs = []
+    for i, fmt in enumerate(("int4_g64", "mxfp4_b32")):
+        d = synth.make_layer(300 + 97 * i, 320, 392, n_outliers=4, outlier_scale=30.0, seed=41 + i)
+        lam, inv = _smooth(d)
+        ref = oracle_weights(d, 16, fmt, lam)
+        bf = lambda a: O.f32_to_bf16_bits(a)
+        lay = w4.W4A4Linear(w4.prepare_weights(d["w"], lam, 16, fmt, bf(ref["l1"]), bf(ref["l2"])), inv)
+        x = torch.from_numpy(np.ascontiguousarray(d["x"]).view(np.int16)).cuda().view(torch.bfloat16)
+        jobs.append((lay, x, torch.cuda.Stream()))
+    print("[threads] int4 + mxfp4 on two streams from two host threads", flush=True)
+    alone = [lay(x).cpu() for lay, x, _ in jobs]
+    torch.cuda.synchronize()
+    got, errors = [[], []], []
+
+    def work(j):
+        lay, x, st = jobs[j]
+        try:
+            with torch.cuda.stream(st):
+                for _ in range(8):
+                    got[j].append(lay(x, stream=st))
+            st.synchronize()
+        except Exception as e:  # reported below: a thread's exception does not fail the test by itself
+            errors.append(e)
+    th = [threading.Thread(target=work, args=(j,)) for j in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errors, errors
+    for j in range(2):
+        assert len(got[j]) == 8
+        for y in got[j]:
+            assert torch.equal(y.cpu(), alone[j]), f"thread {j}: a concurrent call differs from the call made alone"
+
+
 @pytest.mark.parametrize("fmt", ["int4_g64", "mxfp4_b32", "w8a8"])
 def test_graph_capture_and_replay(fmt):
     """The layer step (activation side, then the GEMM) captured once in a HIP graph: the library's
