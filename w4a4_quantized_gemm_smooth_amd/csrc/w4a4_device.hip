@@ -524,6 +524,13 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
                                                     const uint16_t* bias, int M, int N, int m_pad, int m0, int n0,
                                                     int tn, int wm, int wn, int wave, int lane);
 
+// Chunk swizzle of a t row staged in LDS (rows of RP fp32, 16-byte chunks): row r keeps its chunk c
+// at position c ^ t_chunk_sw(r), so that 16-byte reads of one chunk of 32 consecutive rows hit
+// distinct banks (2 ways, the minimum for 64 lanes) where rows two (RP 32) or four (RP 16, 48) apart
+// would otherwise share them.
+template <int RP>
+__device__ __forceinline__ int t_chunk_sw(int r) { return RP == 32 ? (r >> 1) & 7 : (r >> 2) & 3; }
+
 // FUSE < 0: the plain GEMM (fa unused). FUSE >= 0 (INT4 only): fc1 of the MLP with fc2's
 // activation side in the epilogue, FUSE = fc2's rank_pad / 16; Y may then be NULL.
 template <int FMT, int NTR, int FUSE = -1>  // NTR = rank_pad / 16
@@ -630,6 +637,11 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     return byte < TSPLIT ? reinterpret_cast<const uint8_t*>(ring[I4_RING - 2]) + byte
                          : reinterpret_cast<const uint8_t*>(ring[I4_RING - 1]) + (byte - TSPLIT);
   };
+  // Within a staged t row, 16-byte chunk c sits at chunk position c ^ t_chunk_sw(r): the MFMA operand
+  // reads take one chunk of 32 consecutive rows, and rows two (128-byte rows) or four (64- and
+  // 192-byte rows) apart would otherwise share LDS banks. The XOR stays inside the row (8 chunks,
+  // or an aligned group of 4).
+  constexpr int TCH = T_LDS ? TROWB / 16 : 1;  // chunks per t row
   v4i LB[KS][2];
   float4 tv[KS][I4_MT][2];
   auto lr_load = [&](int k0) {  // L2 operands, and t when it is not staged in LDS
@@ -652,41 +664,44 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   };
   // t from its LDS tile, ranks k0 .. k0 + 31 (one or two 16-rank K-steps): one asm block with
   // every read and its own wait (the compiler's LDS-DMA tracking cannot tell slots 4/5 from the
-  // ring groups still in flight and would wait for all of them). Lane address of tile row i: the
-  // row's byte in the tile plus 4 k0 + 32 lh (ranks k0 + 8 lh ..).
+  // ring groups still in flight and would wait for all of them). The lane's rows i = 0..3 (32
+  // apart, one slot) share the chunk swizzle t_chunk_sw(lr): one address per chunk, the rows as
+  // immediate offsets RS·i. Chunk of (K-step s, half h): k0 / 4 + 4 s + 2 lh + h.
   auto t_from_lds = [&](int k0) {
     typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
-    uint32_t ad[I4_MT];
+    constexpr int RS = 32 * TROWB;  // bytes from row i to row i + 1 of the lane
+    const uint32_t row0 = (uint32_t)(uintptr_t)(lds_cptr)t_row_ptr(wm * 128 + lr);
+    const int x = t_chunk_sw<RP>(lr), cb = k0 / 4 + 2 * lh;
+    uint32_t ad[4];
 #pragma unroll
-    for (int i = 0; i < I4_MT; ++i)
-      ad[i] = (uint32_t)(uintptr_t)(lds_cptr)t_row_ptr(wm * 128 + i * 32 + lr) + 4 * k0 + 32 * lh;
+    for (int ci = 0; ci < 4; ++ci) ad[ci] = row0 + 16 * ((cb + (ci & 1) + 4 * (ci >> 1)) ^ x);
     if (RP - k0 >= 32) {
       asm volatile(
-          "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:16\n\t"
-          "ds_read_b128 %2, %16 offset:64\n\tds_read_b128 %3, %16 offset:80\n\t"
-          "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:16\n\t"
-          "ds_read_b128 %6, %17 offset:64\n\tds_read_b128 %7, %17 offset:80\n\t"
-          "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:16\n\t"
-          "ds_read_b128 %10, %18 offset:64\n\tds_read_b128 %11, %18 offset:80\n\t"
-          "ds_read_b128 %12, %19\n\tds_read_b128 %13, %19 offset:16\n\t"
-          "ds_read_b128 %14, %19 offset:64\n\tds_read_b128 %15, %19 offset:80\n\t"
+          "ds_read_b128 %0, %16\n\tds_read_b128 %4, %16 offset:%c20\n\t"
+          "ds_read_b128 %8, %16 offset:%c21\n\tds_read_b128 %12, %16 offset:%c22\n\t"
+          "ds_read_b128 %1, %17\n\tds_read_b128 %5, %17 offset:%c20\n\t"
+          "ds_read_b128 %9, %17 offset:%c21\n\tds_read_b128 %13, %17 offset:%c22\n\t"
+          "ds_read_b128 %2, %18\n\tds_read_b128 %6, %18 offset:%c20\n\t"
+          "ds_read_b128 %10, %18 offset:%c21\n\tds_read_b128 %14, %18 offset:%c22\n\t"
+          "ds_read_b128 %3, %19\n\tds_read_b128 %7, %19 offset:%c20\n\t"
+          "ds_read_b128 %11, %19 offset:%c21\n\tds_read_b128 %15, %19 offset:%c22\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(tv[0][0][0]), "=&v"(tv[0][0][1]), "=&v"(tv[1][0][0]), "=&v"(tv[1][0][1]),
             "=&v"(tv[0][1][0]), "=&v"(tv[0][1][1]), "=&v"(tv[1][1][0]), "=&v"(tv[1][1][1]),
             "=&v"(tv[0][2][0]), "=&v"(tv[0][2][1]), "=&v"(tv[1][2][0]), "=&v"(tv[1][2][1]),
             "=&v"(tv[0][3][0]), "=&v"(tv[0][3][1]), "=&v"(tv[1][3][0]), "=&v"(tv[1][3][1])
-          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(RS), "i"(2 * RS), "i"(3 * RS)
           : "memory");
     } else {
       asm volatile(
-          "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\t"
-          "ds_read_b128 %2, %9\n\tds_read_b128 %3, %9 offset:16\n\t"
-          "ds_read_b128 %4, %10\n\tds_read_b128 %5, %10 offset:16\n\t"
-          "ds_read_b128 %6, %11\n\tds_read_b128 %7, %11 offset:16\n\t"
+          "ds_read_b128 %0, %8\n\tds_read_b128 %2, %8 offset:%c10\n\t"
+          "ds_read_b128 %4, %8 offset:%c11\n\tds_read_b128 %6, %8 offset:%c12\n\t"
+          "ds_read_b128 %1, %9\n\tds_read_b128 %3, %9 offset:%c10\n\t"
+          "ds_read_b128 %5, %9 offset:%c11\n\tds_read_b128 %7, %9 offset:%c12\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(tv[0][0][0]), "=&v"(tv[0][0][1]), "=&v"(tv[0][1][0]), "=&v"(tv[0][1][1]),
             "=&v"(tv[0][2][0]), "=&v"(tv[0][2][1]), "=&v"(tv[0][3][0]), "=&v"(tv[0][3][1])
-          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+          : "v"(ad[0]), "v"(ad[1]), "i"(RS), "i"(2 * RS), "i"(3 * RS)
           : "memory");
     }
   };
@@ -713,7 +728,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     for (int j = 0; j < 2; ++j)
       LBn[j] = *reinterpret_cast<const v4i*>(l2t + (size_t)(n0 + wn * 64 + j * 32 + lr) * RP + 32 + 8 * lh);
   }
-  if (T_LDS) {  // t tile -> the last two slots: TBYTES / 8 bytes per wave, 1 KB per DMA instruction
+  if constexpr (T_LDS) {  // t tile -> the last two slots: TBYTES / 8 bytes per wave, 1 KB per DMA instruction
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     const __amdgpu_buffer_rsrc_t t_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(xl1 + (size_t)m0 * RP), 0, (m_pad - m0) * TROWB, RSRC_W3);
@@ -724,7 +739,10 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
       const int off = wave * TCHUNK + q * 1024;
       uint8_t* dst = off < TSPLIT ? reinterpret_cast<uint8_t*>(ring[I4_RING - 2]) + off
                                   : reinterpret_cast<uint8_t*>(ring[I4_RING - 1]) + (off - TSPLIT);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr_t)dst, 16, 16 * lane, off, 0, 0);
+      // lane: LDS chunk position p of tile row r gets the row's chunk p ^ t_chunk_sw(r)
+      const int slot = off / 16 + lane, r = slot / TCH, pc = slot % TCH;
+      const int src = r * TROWB + 16 * (pc ^ t_chunk_sw<RP>(r));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr_t)dst, 16, src, 0, 0, 0);
     }
   }
 
@@ -738,7 +756,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
   wait_vmcnt<DMA_PER_GROUP * (I4_RING - 3)>();
   __builtin_amdgcn_s_barrier();
   if (NTR > 0) {
-    if (T_LDS) t_from_lds(0);
+    if constexpr (T_LDS) t_from_lds(0);
     lr_mfma(0);
 #pragma unroll
     for (int k0 = 32; k0 < RP; k0 += 32) {
