@@ -524,13 +524,6 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
                                                     const uint16_t* bias, int M, int N, int m_pad, int m0, int n0,
                                                     int tn, int wm, int wn, int wave, int lane);
 
-// Chunk swizzle of a t row staged in LDS (rows of RP fp32, 16-byte chunks): row r keeps its chunk c
-// at position c ^ t_chunk_sw(r), so that 16-byte reads of one chunk of 32 consecutive rows hit
-// distinct banks (2 ways, the minimum for 64 lanes) where rows two (RP 32) or four (RP 16, 48) apart
-// would otherwise share them.
-template <int RP>
-__device__ __forceinline__ int t_chunk_sw(int r) { return RP == 32 ? (r >> 1) & 7 : (r >> 2) & 3; }
-
 // FUSE < 0: the plain GEMM (fa unused). FUSE >= 0 (INT4 only): fc1 of the MLP with fc2's
 // activation side in the epilogue, FUSE = fc2's rank_pad / 16; Y may then be NULL.
 template <int FMT, int NTR, int FUSE = -1>  // NTR = rank_pad / 16
@@ -637,10 +630,7 @@ __global__ __launch_bounds__(I4_THREADS) void gemm_kernel(
     return byte < TSPLIT ? reinterpret_cast<const uint8_t*>(ring[I4_RING - 2]) + byte
                          : reinterpret_cast<const uint8_t*>(ring[I4_RING - 1]) + (byte - TSPLIT);
   };
-  // Within a staged t row, 16-byte chunk c sits at chunk position c ^ t_chunk_sw(r): the MFMA operand
-  // reads take one chunk of 32 consecutive rows, and rows two (128-byte rows) or four (64- and
-  // 192-byte rows) apart would otherwise share LDS banks. The XOR stays inside the row (8 chunks,
-  // or an aligned group of 4).
+  // Within a staged t row, 16-byte chunk c sits at chunk position c ^ t_chunk_sw(r) (LDS banks)
   constexpr int TCH = T_LDS ? TROWB / 16 : 1;  // chunks per t row
   v4i LB[KS][2];
   float4 tv[KS][I4_MT][2];
@@ -1170,6 +1160,7 @@ __global__ __launch_bounds__(MX_THREADS, 2) void gemm_mx_small_kernel(
   // copies; larger ranks load t directly.
   constexpr bool T_LDS = NTR > 0 && NTR <= 2;
   constexpr int TROWB = RP * 4;
+  constexpr int TCH = T_LDS ? TROWB / 16 : 1;  // 16-byte chunks per t row
   static_assert(!T_LDS || 64 * TROWB <= (int)sizeof(MxSlot), "half the t tile fits a slot");
   auto lr_load = [&](int k0) {  // L2 operands, and t when it is not staged in LDS
 #pragma unroll
@@ -1191,34 +1182,36 @@ __global__ __launch_bounds__(MX_THREADS, 2) void gemm_mx_small_kernel(
   };
   // t from its LDS tile: one asm block with every read and its own wait (the compiler's LDS-DMA
   // tracking cannot tell slots 6/7 from the ring groups still in flight and would wait for all of
-  // them). Lane address of tile row i: the row's byte in its slot plus 32 lh (ranks 8 lh ..).
+  // them). The lane's rows wm * 64 + lr + 32 i (i = 0, 1: one slot, 32 rows apart) share the chunk
+  // swizzle t_chunk_sw(lr): one address per chunk, the second row as an immediate offset. Chunk
+  // of (K-step s, half h): 4 s + 2 lh + h.
   auto t_from_lds = [&]() {
     typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
-    uint32_t ad[MX_MT];
+    constexpr int RS = 32 * TROWB;  // bytes from row i = 0 to row i = 1 of the lane
+    const uint8_t* slot = reinterpret_cast<const uint8_t*>(wm ? ring[7] : ring[6]);
+    const uint32_t row0 = (uint32_t)(uintptr_t)(lds_cptr)(slot + lr * TROWB);
+    const int x = t_chunk_sw<RP>(lr);
+    uint32_t ad[4];
 #pragma unroll
-    for (int i = 0; i < MX_MT; ++i) {
-      const int r = arow0 + i * 32;  // wm * 64 + 32 i + lr: slot 6 for wm == 0, slot 7 for wm == 1
-      const uint8_t* slot = reinterpret_cast<const uint8_t*>((r >> 6) ? ring[7] : ring[6]);
-      ad[i] = (uint32_t)(uintptr_t)(lds_cptr)(slot + (r & 63) * TROWB) + 32 * lh;
-    }
+    for (int ci = 0; ci < 4; ++ci) ad[ci] = row0 + 16 * ((2 * lh + (ci & 1) + 4 * (ci >> 1)) ^ x);
     if constexpr (NTR == 2) {
       asm volatile(
-          "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\t"
-          "ds_read_b128 %2, %8 offset:64\n\tds_read_b128 %3, %8 offset:80\n\t"
-          "ds_read_b128 %4, %9\n\tds_read_b128 %5, %9 offset:16\n\t"
-          "ds_read_b128 %6, %9 offset:64\n\tds_read_b128 %7, %9 offset:80\n\t"
+          "ds_read_b128 %0, %8\n\tds_read_b128 %4, %8 offset:%c12\n\t"
+          "ds_read_b128 %1, %9\n\tds_read_b128 %5, %9 offset:%c12\n\t"
+          "ds_read_b128 %2, %10\n\tds_read_b128 %6, %10 offset:%c12\n\t"
+          "ds_read_b128 %3, %11\n\tds_read_b128 %7, %11 offset:%c12\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(tv[0][0][0]), "=&v"(tv[0][0][1]), "=&v"(tv[1][0][0]), "=&v"(tv[1][0][1]),
             "=&v"(tv[0][1][0]), "=&v"(tv[0][1][1]), "=&v"(tv[1][1][0]), "=&v"(tv[1][1][1])
-          : "v"(ad[0]), "v"(ad[1])
+          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(RS)
           : "memory");
     } else if constexpr (NTR == 1) {
       asm volatile(
-          "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\t"
-          "ds_read_b128 %2, %5\n\tds_read_b128 %3, %5 offset:16\n\t"
+          "ds_read_b128 %0, %4\n\tds_read_b128 %2, %4 offset:%c6\n\t"
+          "ds_read_b128 %1, %5\n\tds_read_b128 %3, %5 offset:%c6\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(tv[0][0][0]), "=&v"(tv[0][0][1]), "=&v"(tv[0][1][0]), "=&v"(tv[0][1][1])
-          : "v"(ad[0]), "v"(ad[1])
+          : "v"(ad[0]), "v"(ad[1]), "i"(RS)
           : "memory");
     }
   };
@@ -1248,7 +1241,10 @@ __global__ __launch_bounds__(MX_THREADS, 2) void gemm_mx_small_kernel(
     for (int q = 0; q < TCHUNK / 1024; ++q) {
       const int off = wave * TCHUNK + q * 1024;  // byte of the tile; rows 0..63 in slot 6
       uint8_t* dst = reinterpret_cast<uint8_t*>(off >= 64 * TROWB ? ring[7] : ring[6]) + (off % (64 * TROWB));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr_t)dst, 16, 16 * lane, off, 0, 0);
+      // lane: LDS chunk position p of tile row r gets the row's chunk p ^ t_chunk_sw(r)
+      const int slot = off / 16 + lane, r = slot / TCH, pc = slot % TCH;
+      const int src = r * TROWB + 16 * (pc ^ t_chunk_sw<RP>(r));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr_t)dst, 16, src, 0, 0, 0);
     }
   }
 #pragma unroll

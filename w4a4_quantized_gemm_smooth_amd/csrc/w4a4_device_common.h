@@ -56,6 +56,15 @@ constexpr int I4_NS = 8;            // ring slots (K steps); even
 // the 16-byte reads of 8 consecutive lanes cover all 64 banks)
 __device__ __forceinline__ int sw_off32(int r, int h) { return r * 32 + 16 * (h ^ ((r >> 3) & 1)); }
 
+// Chunk swizzle of a t row staged in LDS (rows of RP fp32, 16-byte chunks): row r keeps its chunk c
+// at position c ^ t_chunk_sw(r), so that 16-byte reads of one chunk of 32 consecutive rows hit
+// distinct banks (2 ways, the minimum for 64 lanes) where rows two (RP 32) or four (RP 16, 48) apart
+// would otherwise share them. The XOR stays inside the row (8 chunks, or an aligned group of 4).
+// Compute it into a local before passing it to a builtin: as a call inside the argument list of
+// the LDS-DMA builtin in a kernel template, the host pass drops the kernel's launch stubs.
+template <int RP>
+__device__ __forceinline__ int t_chunk_sw(int r) { return RP == 32 ? (r >> 1) & 7 : (r >> 2) & 3; }
+
 // Tile order. Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8),
 // so consecutive logical tiles are handed to the same XCD; logical tiles then sweep N in groups of
 // I4_GROUP_M M-tiles, so the blocks an XCD runs together share A and B slices in its L2.

@@ -151,6 +151,8 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
   constexpr int RP = NTR * 16, KS = 2;
   constexpr bool T_LDS = !MX && NTR > 0 && NTR <= 2;
   constexpr int TROWB = RP * 4;  // bytes of one t row
+  // staged t rows (either tile below) keep 16-byte chunk c at position c ^ t_chunk_sw(r) (LDS banks)
+  constexpr int T_CHUNKS = RP > 0 ? TROWB / 16 : 1;  // chunks per t row
   constexpr int NDMA_STEP = MX ? 5 : 4;  // copies per DMA wave and step
   __shared__ __attribute__((aligned(16))) Slot sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7;
   __shared__ __attribute__((aligned(16))) uint8_t t_tile[T_LDS ? 256 * TROWB : 16];
@@ -238,16 +240,20 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
         const int off = dw * TCH + q * 1024;  // chunks never straddle the 16 KB split
         uint8_t* dst = off < 16384 ? reinterpret_cast<uint8_t*>(ring[6]) + off
                                    : reinterpret_cast<uint8_t*>(ring[7]) + (off - 16384);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr)dst, 16, 16 * lane, off, 0, 0);
+        const int slot = off / 16 + lane, r = slot / T_CHUNKS, pc = slot % T_CHUNKS;
+        const int src = r * TROWB + 16 * (pc ^ t_chunk_sw<RP>(r));  // position pc gets chunk pc ^ sw(r)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr)dst, 16, src, 0, 0, 0);
       }
     }
-    if (T_LDS) {  // t tile -> its LDS area, 1 KB per DMA instruction
+    if constexpr (T_LDS) {  // t tile -> its LDS area, 1 KB per DMA instruction
       const __amdgpu_buffer_rsrc_t t_rsrc = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(xl1 + (size_t)m0 * RP), 0, (m_pad - m0) * TROWB, RSRC_W3);
 #pragma unroll
       for (int q = 0; q < TCHUNK / 1024; ++q) {
         const int off = dw * TCHUNK + q * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr)(t_tile + off), 16, 16 * lane, off, 0, 0);
+        const int slot = off / 16 + lane, r = slot / T_CHUNKS, pc = slot % T_CHUNKS;
+        const int src = r * TROWB + 16 * (pc ^ t_chunk_sw<RP>(r));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(t_rsrc, (lds_ptr)(t_tile + off), 16, src, 0, 0, 0);
       }
     }
     // prologue: steps 0 .. NS-3 in flight; the t tile and step 0 landed
@@ -297,8 +303,11 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
       for (int s2 = 0; s2 < RP / 16; ++s2)
 #pragma unroll
         for (int i = 0; i < I4_MT; ++i) {
-          const float* tp = reinterpret_cast<const float*>(t_row_lds(wm * 128 + i * 32 + lr)) + 16 * s2 + 8 * lh;
-          const float4 t0 = *reinterpret_cast<const float4*>(tp), t1 = *reinterpret_cast<const float4*>(tp + 4);
+          const int r = wm * 128 + i * 32 + lr;
+          const uint8_t* tp = t_row_lds(r);
+          const int c = 4 * s2 + 2 * lh, x = t_chunk_sw<RP>(r);  // the row's chunks c, c + 1
+          const float4 t0 = *reinterpret_cast<const float4*>(tp + 16 * (c ^ x));
+          const float4 t1 = *reinterpret_cast<const float4*>(tp + 16 * ((c + 1) ^ x));
           const v4i TA = v4i{(int)pack_bf16x2(t0.x, t0.y), (int)pack_bf16x2(t0.z, t0.w), (int)pack_bf16x2(t1.x, t1.y),
                              (int)pack_bf16x2(t1.z, t1.w)};
 #pragma unroll
@@ -405,9 +414,17 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_w8a8_kernel(
 #pragma unroll
         for (int i = 0; i < I4_MT; ++i) {
           const int r = wm * 128 + i * 32 + lr;
-          const float* tp = T_LDS ? reinterpret_cast<const float*>(t_tile + r * TROWB) + kk + 8 * lh
-                                  : xl1 + (size_t)(m0 + r) * RP + kk + 8 * lh;
-          const float4 t0 = *reinterpret_cast<const float4*>(tp), t1 = *reinterpret_cast<const float4*>(tp + 4);
+          float4 t0, t1;
+          if constexpr (T_LDS) {  // the row's chunks c, c + 1 at their swizzled positions
+            const uint8_t* tr = t_tile + r * TROWB;
+            const int c = kk / 4 + 2 * lh, x = t_chunk_sw<RP>(r);
+            t0 = *reinterpret_cast<const float4*>(tr + 16 * (c ^ x));
+            t1 = *reinterpret_cast<const float4*>(tr + 16 * ((c + 1) ^ x));
+          } else {
+            const float* tp = xl1 + (size_t)(m0 + r) * RP + kk + 8 * lh;
+            t0 = *reinterpret_cast<const float4*>(tp);
+            t1 = *reinterpret_cast<const float4*>(tp + 4);
+          }
           const v4i TA = v4i{(int)pack_bf16x2(t0.x, t0.y), (int)pack_bf16x2(t0.z, t0.w), (int)pack_bf16x2(t1.x, t1.y),
                              (int)pack_bf16x2(t1.z, t1.w)};
 #pragma unroll
