@@ -437,8 +437,8 @@ def main():
                          "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's multi-GPU sharding "
-              "is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the layer's multi-GPU sharding "
+              "(token-, column- or row-parallel) is not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch
