@@ -163,6 +163,8 @@ def test_ragged_shapes_with_bias(fmt, shape):
     (300, 256, 260, 16),
     (2000, 1088, 8440, 16),   # 17 groups: two full rounds of the GEMM's 8-slot LDS ring and a partial one,
                               # on 8 x 33 = 264 output tiles (more than the GPU runs at once), ragged M and N
+    (300, 256, 260, 32),      # t tile staged in LDS with 128-byte rows (two 16-rank steps per read)
+    (520, 1088, 600, 48),     # 192-byte t rows (a two-step and a one-step read), ragged tiles
 ])
 def test_exact_arithmetic_layer_bit_exact(shape):
     """λ = 1, power-of-two scales, representable X̂ and R, one-hot L1: every rounding is exact, so
@@ -186,6 +188,8 @@ def test_exact_arithmetic_layer_bit_exact(shape):
     (300, 1088, 260, 16),     # small-grid kernel, 17 groups (the 8-slot ring wraps twice)
     (2000, 1088, 8440, 16),   # large-grid kernel (16 x 66 blocks of 128²), up projection before the loop
     (1000, 256, 8440, 40),    # large-grid kernel, rank > 32: up projection in the epilogue
+    (300, 1088, 260, 32),     # small-grid kernel, t tile staged with 128-byte rows
+    (2000, 256, 8440, 32),    # large-grid kernel, t tile staged with 128-byte rows
 ])
 def test_mxfp4_exact_arithmetic_layer_bit_exact(shape):
     """MXFP4 counterpart: E2M1 values times a power of two per 32-block with a ±6 in every block
