@@ -210,6 +210,30 @@ def test_mxfp4_exact_arithmetic_layer_bit_exact(shape):
     assert np.all(g["y"][:, n:] == -7.0)
 
 
+@pytest.mark.parametrize("shape", [
+    (64, 256, 96, 0),         # no low-rank branch
+    (300, 512, 260, 16),      # t tile staged in LDS (64-byte rows)
+    (2000, 512, 8440, 32),    # 128-byte t rows, 8 x 33 = 264 output tiles, ragged M and N
+    (520, 256, 600, 48),      # rank > 32: t read from global memory in the epilogue
+])
+def test_w8a8_exact_arithmetic_layer_bit_exact(shape):
+    """8-bit setting: per-row powers of two as the per-token and per-channel scales, λ = 1, one-hot
+    L1; the int32 products and every fp32 step of the epilogue are exact, so Y is bit-exact."""
+    from test_oracle_pins import w8_exact_case
+    m, k, n, r = shape
+    c = w8_exact_case(m, k, n, r, seed=m + k)
+    lam = np.ones(k, np.float32)
+    ref = O.prepare_weights(c["w_bits"], lam, r, "w8a8", l1=c["l1"], l2=c["l2"])
+    d = dict(x=c["x_bits"], w=c["w_bits"])
+    print(f"[exact w8a8] M={m} K={k} N={n} r={r}", flush=True)
+    g = gpu_layer(d, lam, lam, r, "w8a8", ref, pad_cols=3)
+    check_activation_side(d, lam, ref, "w8a8", g)
+    y_ref = O.linear(c["x_bits"], lam, ref)["y"]
+    assert np.array_equal(y_ref, O.bf16_rne(c["y_exact"].astype(np.float32)))
+    assert np.array_equal(g["y"][:, :n], y_ref)
+    assert np.all(g["y"][:, n:] == -7.0)
+
+
 def test_zero_and_tiny_activations():
     """All-zero rows and groups whose scale would be subnormal give zero codes and zero scales."""
     d = synth.make_layer(64, 256, 128, n_outliers=2, outlier_scale=30.0, seed=4)

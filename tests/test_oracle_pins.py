@@ -558,6 +558,36 @@ def mx_exact_case(m=64, k=128, n=96, r=2, seed=5):
                 y_exact=y, rank=r)
 
 
+def w8_exact_case(m=64, k=256, n=96, r=2, seed=7):
+    """The 8-bit setting's counterpart of ``exact_case``: row m of X is q·2^e_m with integer
+    |q| <= 127 and a +127 and a -127 in every row, so the per-token scale is exactly 2^e_m; the
+    residual's rows are q·2^-9 built the same way (per-channel scale 2^-9); λ = 1, one-hot L1 and
+    L2 in {-1/8, 0, 1/8}, so W stays bf16-representable. In units of 2^(e_m - 9) the main term is
+    the integer dot product (at most K·127²) and each low-rank term at most 127·64, so with the sum
+    asserted below 2^24 units every fp32 partial sum is exact and Y is reproduced bit for bit."""
+    rng = np.random.default_rng(seed)
+    ex = rng.integers(-3, 3, size=m)
+    qx = _force_full_scale(rng.integers(-127, 128, size=(m, k)), rng, k, 127)
+    x = qx * (2.0 ** ex)[:, None]
+    qw = _force_full_scale(rng.integers(-127, 128, size=(n, k)), rng, k, 127)
+    resid = qw * 2.0 ** -9
+    sel = rng.choice(k, r, replace=False)
+    l1 = np.zeros((k, r))
+    l1[sel, np.arange(r)] = 1.0
+    l2 = rng.integers(-1, 2, size=(r, n)) * 0.125
+    w = resid + (l1 @ l2).T
+    bits = lambda a: O.f32_to_bf16_bits(a.astype(np.float32))
+    assert np.array_equal(O.bf16_bits_to_f32(bits(x)), x) and np.array_equal(O.bf16_bits_to_f32(bits(w)), w)
+    assert k * 127 * 127 + r * 127 * 64 < 2 ** 24
+    y = x @ resid.T + x[:, sel] @ l2                   # dyadic, exact in fp64
+    for i, j in ((0, 0), (m - 1, n - 1), (m // 2, n // 3)):
+        fr = sum(Fraction(float(x[i, kk])) * Fraction(float(resid[j, kk])) for kk in range(k)) + \
+            sum(Fraction(float(x[i, sel[t]])) * Fraction(float(l2[t, j])) for t in range(r))
+        assert Fraction(float(y[i, j])) == fr
+    return dict(x_bits=bits(x), w_bits=bits(w), l1=l1.astype(np.float32), l2=l2.astype(np.float32),
+                y_exact=y, rank=r)
+
+
 def test_exact_case_end_to_end():
     c = exact_case()
     lam = np.ones(128, np.float32)
@@ -583,6 +613,19 @@ def test_mx_exact_case_end_to_end():
 
 
 # ---------------------------------------------------------------- LoRA merge (§4.2 / §5.2)
+
+def test_w8_exact_case_end_to_end():
+    c = w8_exact_case(m=40, k=256, n=72, r=3)
+    lam = np.ones(256, np.float32)
+    prep = O.prepare_weights(c["w_bits"], lam, c["rank"], O.FMT_W8A8, l1=c["l1"], l2=c["l2"])
+    out = O.linear(c["x_bits"], lam, prep)
+    assert np.array_equal(out["y_m"] + out["y_l"], c["y_exact"])
+    assert np.array_equal(out["y"], O.bf16_rne(c["y_exact"].astype(np.float32)))
+    # the scales are the constructed powers of two and the codes the constructed integers
+    x = O.bf16_bits_to_f32(c["x_bits"]).astype(np.float64)
+    assert np.all(np.log2(out["sx"]) % 1 == 0) and np.all(prep["sw"] == np.float32(2.0 ** -9))
+    assert np.array_equal(out["cx"].astype(np.float64) * out["sx"][:, None], x)
+    assert np.abs(out["cx"]).max() == 127 and np.abs(prep["cw"]).max() == 127
 def test_lora_merge_adds_exactly_the_lora_term():
     d = synth.make_layer(64, 256, 128, n_outliers=4, outlier_scale=30.0, seed=7, lora_rank=16)
     x = O.bf16_bits_to_f32(d["x"])
