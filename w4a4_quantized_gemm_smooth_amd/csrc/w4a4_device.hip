@@ -103,18 +103,37 @@ __device__ __forceinline__ uint32_t gelu_tab_lookup(uint32_t b, const uint16_t* 
 __device__ __forceinline__ uint32_t gelu_any(uint32_t b, const uint16_t* tab) {
   return gelu_off(b) < (uint32_t)GELU_SIGN ? gelu_tab_lookup(b, tab) : bf16_rne(gelu32(bf16f(b)));
 }
-// N inputs at once: the plain lookups when every input of the lane is in the table's range
-template <int N>
-__device__ __forceinline__ void gelu_n(uint32_t (&b)[N], const uint16_t* tab) {
-  bool all_in = true;
+// 2 NW inputs packed two to a word (input 2e in the low half of w[e]) -> b[2e], b[2e + 1], the
+// same values as gelu_any of each: the plain lookups when every input of the lane is in the
+// table's range. The offsets, their range check and the table byte offsets (below 14 KB) are
+// formed two inputs at a time with packed 16-bit integer operations; the table's LDS address is
+// added per input.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <int NW>
+__device__ __forceinline__ void gelu_pk(const uint32_t (&w)[NW], uint32_t (&b)[2 * NW], const uint16_t* tab) {
+  typedef __attribute__((address_space(3))) const uint16_t* lds_u16;
+  constexpr unsigned short E0 = GELU_E0 << 7, SIGN_BYTES = 2 * GELU_SIGN;
+  u16x2 off[NW], mx = {0, 0};
 #pragma unroll
-  for (int e = 0; e < N; ++e) all_in &= gelu_off(b[e]) < (uint32_t)GELU_SIGN;
-  if (all_in) {
+  for (int e = 0; e < NW; ++e) {
+    off[e] = __builtin_bit_cast(u16x2, w[e] & 0x7FFF7FFFu) - u16x2{E0, E0};  // gelu_off of both halves
+    mx = __builtin_elementwise_max(mx, off[e]);
+  }
+  if (mx.x < GELU_SIGN && mx.y < GELU_SIGN) {
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_u16)tab;
 #pragma unroll
-    for (int e = 0; e < N; ++e) b[e] = gelu_tab_lookup(b[e], tab);
+    for (int e = 0; e < NW; ++e) {
+      const u16x2 sgn = __builtin_bit_cast(u16x2, w[e]) >> (unsigned short)15;
+      const u16x2 byte = (off[e] << (unsigned short)1) + sgn * u16x2{SIGN_BYTES, SIGN_BYTES};
+      b[2 * e] = *(lds_u16)(uintptr_t)(base + byte.x);
+      b[2 * e + 1] = *(lds_u16)(uintptr_t)(base + byte.y);
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < N; ++e) b[e] = gelu_any(b[e], tab);
+    for (int e = 0; e < NW; ++e) {
+      b[2 * e] = gelu_any(w[e] & 0xFFFFu, tab);
+      b[2 * e + 1] = gelu_any(w[e] >> 16, tab);
+    }
   }
 }
 
@@ -218,12 +237,18 @@ __device__ __forceinline__ void scale_pair(const float (&ua)[16], const float (&
 template <bool GELU_IN>
 __device__ __forceinline__ void unpack16(const v4i (&xv)[2], float (&u)[16], const uint16_t* gtab) {
   uint32_t bits[16];
+  if constexpr (GELU_IN) {
+    uint32_t w[8];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const uint32_t w = (uint32_t)xv[e >> 3][(e >> 1) & 3];
-    bits[e] = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+    for (int q = 0; q < 8; ++q) w[q] = (uint32_t)xv[q >> 2][q & 3];
+    gelu_pk(w, bits, gtab);  // the 16 table reads go out together
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t w = (uint32_t)xv[e >> 3][(e >> 1) & 3];
+      bits[e] = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+    }
   }
-  if constexpr (GELU_IN) gelu_n(bits, gtab);  // the 16 table reads go out together
 #pragma unroll
   for (int e = 0; e < 16; ++e) u[e] = bf16f(bits[e]);
 }
@@ -977,14 +1002,13 @@ __device__ __forceinline__ void gelu_quant_epilogue(v16f (&acc)[I4_MT][2], uint8
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j) {  // one 32 x 32 tile (16 values of the lane) at a time
+        uint32_t yw[8];
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const uint32_t y = pack_bf16x2(acc[2 * half + ii][j][v] + bcol[j], acc[2 * half + ii][j][v + 1] + bcol[j]);
-          gx[ii][j][v] = y & 0xFFFFu;
-          gx[ii][j][v + 1] = y >> 16;
-        }
-    gelu_n(*reinterpret_cast<uint32_t(*)[64]>(&gx[0][0][0]), gtab);
+        for (int v = 0; v < 16; v += 2)
+          yw[v / 2] = pack_bf16x2(acc[2 * half + ii][j][v] + bcol[j], acc[2 * half + ii][j][v + 1] + bcol[j]);
+        gelu_pk(yw, gx[ii][j], gtab);
+      }
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
